@@ -1,0 +1,139 @@
+/*
+ * lce.h -- C ABI of the fused, chunked linear-cross-entropy library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (page "分块交叉熵：从输出投影开始省保存量", glenzli.com,
+ * section 01 "SAME OBJECTIVE", objective equation):
+ *
+ *   Z_ij = H_i . W_j + b_j                 H[N,D], W[V,D], b[V] (b = 0 if absent)
+ *   a_i  = 1[mask_i] * 1[y_i != ignore]    C = sum_i a_i
+ *   L    = (1/C) sum_{a_i=1} ( log sum_j exp(Z_ij) - Z_{i,y_i} )
+ *
+ * computed in T x B score tiles that never form the N x V logits: the forward
+ * pass keeps a running row max m and exp-sum s over vocabulary tiles and
+ * captures the target score from the tile that holds it (section 02 "RUNNING
+ * LSE"); the backward pass replays every tile, rebuilds
+ * p = exp((Z - m) - log s), forms G = (lambda a_i / C)(p - onehot(y)) and
+ * returns dH = G W, dW = G^T H, db = sum_i G_i (section 04 "RECONSTRUCT AND
+ * SUM").  Prompt rows (label == ignore or mask false) never enter the
+ * projection (ChunkedLinearCrossEntropy page, m.nxbn.cn, section on filtering
+ * tokens with label -100).
+ *
+ * Conventions for every call
+ *  - Device arrays are contiguous, row-major, 16-byte aligned.  H, W and b
+ *    share one element type (lce_dtype_t); the projection runs in that type
+ *    with fp32 accumulation, the scores Z and every statistic are fp32.
+ *  - D must be a multiple of 8 (bf16) or 4 (fp32).
+ *  - The caller owns all memory, including the workspace (size it with
+ *    lce_workspace_size).  The library never allocates device memory and keeps
+ *    no state between calls (apart from the optional profiling switch at the
+ *    end of this header).  Inputs are never written.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream).
+ *    Only lce_compact_valid synchronises the stream (to return C).
+ *  - No exception crosses the ABI; every call returns an lce_status_t.
+ *  - Calls that share a workspace must not overlap in time.
+ */
+#ifndef LCE_H_
+#define LCE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LCE_DTYPE_F32 = 0,  /* IEEE binary32 */
+  LCE_DTYPE_BF16 = 1  /* bfloat16 (8 exponent bits, 7 stored mantissa bits) */
+} lce_dtype_t;
+
+typedef enum {
+  LCE_OK = 0,
+  LCE_OK_EMPTY = 1,        /* C == 0: zero loss sentinel / zero gradients written
+                              (section 01: the mean is undefined, the caller
+                              should skip the optimizer step) */
+  LCE_ERR_ARG = -1,        /* null or inconsistent argument, misaligned pointer */
+  LCE_ERR_LABEL = -2,      /* a supervised label lies outside [0, V) */
+  LCE_ERR_WORKSPACE = -3,  /* ws_bytes below lce_workspace_size(...) */
+  LCE_ERR_HIP = -4,        /* a HIP runtime call or kernel launch failed */
+  LCE_ERR_UNSUPPORTED = -5 /* shape outside the documented limits */
+} lce_status_t;
+
+/* Bytes of device workspace that lce_compact_valid, lce_forward and
+ * lce_backward need for these sizes (worst case C = N).  It never grows with
+ * N x V: the largest pieces are the gathered supervised rows (N x D), one
+ * vocabulary chunk of the softmax-gradient tile store (N x min(V, 32768)) and
+ * the fp32 dH accumulators (at most 4 x N x D).  Returns 0 for invalid sizes. */
+size_t lce_workspace_size(int64_t N, int64_t D, int64_t V, lce_dtype_t dt);
+
+/* Valid-token compaction (section 01 definition of a_i and C; the
+ * ChunkedLinearCrossEntropy page's prompt filtering).
+ *   labels       int64[N] device; label of each position.
+ *   mask         uint8[N] device or NULL (NULL = every position masked in);
+ *                nonzero = supervised.
+ *   ignore_index label value that marks an unsupervised position (-100).
+ *   valid_idx    int32[N] device, written: the C supervised positions in
+ *                ascending order in valid_idx[0..C).  Entries >= C untouched.
+ *   C_host       host int64, written: C.
+ * Checks on the device that every supervised label lies in [0, V); if not,
+ * returns LCE_ERR_LABEL (valid_idx contents then unspecified).
+ * Synchronises `stream` once.  Returns LCE_OK, LCE_OK_EMPTY when C == 0. */
+lce_status_t lce_compact_valid(const int64_t* labels, const uint8_t* mask, int64_t N,
+                               int64_t V, int64_t ignore_index, int32_t* valid_idx,
+                               int64_t* C_host, void* ws, size_t ws_bytes, void* stream);
+
+/* Forward pass (sections 01-02).
+ *   H [N,D], W [V,D], b [V] or NULL: device, element type dt.
+ *   labels int64[N], valid_idx int32[C] (from lce_compact_valid), C, N, D, V.
+ *   loss      float[1] device, written: mean CE over the C supervised rows.
+ *   m, logs   float[N] device, written: the saved statistics.  For supervised
+ *             row i, m[i] = max_j Z_ij and logs[i] = log sum_j exp(Z_ij - m[i]);
+ *             unsupervised rows keep the recurrence's initial state
+ *             (m = -inf, logs = -inf).
+ *   row_loss  float[N] device or NULL; if given, written with the per-row CE
+ *             (m - Z_{i,y_i}) + logs for supervised rows and 0 elsewhere.
+ * C == 0: loss = 0, m = logs = -inf, row_loss = 0, returns LCE_OK_EMPTY.
+ * A NaN score makes the loss NaN (it is never hidden). */
+lce_status_t lce_forward(const void* H, const void* W, const void* b, const int64_t* labels,
+                         const int32_t* valid_idx, int64_t C, int64_t N, int64_t D, int64_t V,
+                         lce_dtype_t dt, float* loss, float* m, float* logs, float* row_loss,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/* Backward pass (section 04).
+ *   Same H, W, b, labels, valid_idx, C, N, D, V, dt as the forward call, and
+ *   the m / logs it wrote.
+ *   grad_loss float[1] device or NULL: lambda = dJ/dL (NULL means 1).
+ *   dH [N,D], dW [V,D]: device, type dt, fully overwritten (not accumulated);
+ *   rows of dH for unsupervised positions are exactly 0.
+ *   db [V] device, type dt, or NULL (skip the bias gradient).
+ * Deterministic: the same inputs give bitwise-identical outputs (ordered
+ * reductions, no floating-point atomics).
+ * C == 0: dH, dW and db are zero-filled, returns LCE_OK_EMPTY. */
+lce_status_t lce_backward(const void* H, const void* W, const void* b, const int64_t* labels,
+                          const int32_t* valid_idx, int64_t C, int64_t N, int64_t D, int64_t V,
+                          lce_dtype_t dt, const float* m, const float* logs,
+                          const float* grad_loss, void* dH, void* dW, void* db, void* ws,
+                          size_t ws_bytes, void* stream);
+
+/* Static string for a status code. */
+const char* lce_status_string(lce_status_t status);
+
+/* ---- Optional kernel timing (benchmarks only; not thread-safe) -------------
+ * lce_profile_start(max_launches) makes every following launch record a HIP
+ * event pair on its stream (up to max_launches launches); lce_profile_stop()
+ * synchronises those events and folds them into per-kernel totals, and turns
+ * recording off.  lce_profile_count() gives the number of distinct kernels
+ * seen; lce_profile_entry(i, ...) copies kernel i's name, total milliseconds
+ * and launch count.  Returns LCE_ERR_HIP if an event call fails. */
+lce_status_t lce_profile_start(int32_t max_launches);
+lce_status_t lce_profile_stop(void);
+int32_t lce_profile_count(void);
+lce_status_t lce_profile_entry(int32_t i, char* name, int32_t name_cap, double* total_ms,
+                               int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LCE_H_ */

@@ -1,0 +1,488 @@
+// Host side of the C ABI declared in include/lce.h: argument checks,
+// workspace layout, launch sequencing on the caller's stream, status codes.
+// No device memory is allocated here; the caller passes the workspace.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "lce.h"
+#include "lce_kernels.h"
+
+using namespace lce;
+
+namespace {
+
+constexpr int64_t kVcMax = 32768;     // vocabulary chunk of the gradient tile store
+constexpr int kMaxSplit = 64;         // vocabulary splits of the forward pass
+constexpr int kMaxDhSlots = 4;        // k-splits of the dH GEMM
+constexpr int kCUs = 256;             // MI355X compute units (one 512-thread workgroup each)
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t rup(int64_t a, int64_t b) { return cdiv(a, b) * b; }
+size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// ------------------------------------------------------------------ profiling
+struct Prof {
+  bool on = false;
+  int max = 0, used = 0, pending_kid = -1;
+  std::vector<hipEvent_t> ev;
+  std::vector<int> kid;
+  std::vector<std::string> names;
+  std::vector<double> ms;
+  std::vector<int64_t> cnt;
+};
+Prof g_prof;
+
+void prof_begin(const char* name, hipStream_t s) {
+  Prof& p = g_prof;
+  p.pending_kid = -1;
+  if (!p.on || p.used >= p.max) return;
+  int id = -1;
+  for (size_t i = 0; i < p.names.size(); ++i)
+    if (p.names[i] == name) id = (int)i;
+  if (id < 0) {
+    id = (int)p.names.size();
+    p.names.push_back(name);
+    p.ms.push_back(0.0);
+    p.cnt.push_back(0);
+  }
+  if (hipEventRecord(p.ev[2 * p.used], s) != hipSuccess) return;
+  p.pending_kid = id;
+}
+void prof_end(hipStream_t s) {
+  Prof& p = g_prof;
+  if (p.pending_kid < 0) return;
+  if (hipEventRecord(p.ev[2 * p.used + 1], s) == hipSuccess) {
+    p.kid[p.used] = p.pending_kid;
+    p.used++;
+  }
+  p.pending_kid = -1;
+}
+
+#define LCE_LAUNCH(name, kernel, grid, block, shmem, stream, ...)                  \
+  do {                                                                             \
+    prof_begin(name, stream);                                                      \
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(block), shmem, stream, __VA_ARGS__); \
+    hipError_t e_ = hipGetLastError();                                             \
+    prof_end(stream);                                                              \
+    if (e_ != hipSuccess) return LCE_ERR_HIP;                                      \
+  } while (0)
+
+// ------------------------------------------------------------------ layout
+template <typename T> struct Tile {
+  static constexpr int BM = Cfg<T>::BM;  // vocabulary tile (forward) / M tile (gradients)
+  static constexpr int BN = Cfg<T>::BN;  // row block
+};
+
+struct Layout {
+  // compaction
+  size_t counts, bad, offsets, stat;
+  // shared by forward and backward
+  size_t hc, yc;
+  // forward
+  size_t pm, ps, tgt, lrow;
+  // backward
+  size_t mc, lsc, inv, G, slots, dbp;
+  size_t total;
+  int64_t Npad, Vpad, Vc, nblk;
+};
+
+bool make_layout(int64_t N, int64_t D, int64_t V, lce_dtype_t dt, Layout& L) {
+  if (N < 0 || D <= 0 || V <= 0) return false;
+  if (dt != LCE_DTYPE_F32 && dt != LCE_DTYPE_BF16) return false;
+  const int64_t esz = dt == LCE_DTYPE_BF16 ? 2 : 4;
+  const int64_t bn = dt == LCE_DTYPE_BF16 ? Tile<uint16_t>::BN : Tile<float>::BN;
+  L.Npad = rup(std::max<int64_t>(N, 1), 256);
+  L.nblk = cdiv(std::max<int64_t>(N, 1), kCmpBlock);
+  L.Vpad = rup(V, 256);
+  L.Vc = std::min<int64_t>(L.Vpad, kVcMax);
+  size_t off = 0;
+  auto take = [&](int64_t bytes) {
+    const size_t o = off;
+    off = a256(off + (size_t)bytes);
+    return o;
+  };
+  L.counts = take(L.nblk * 4);
+  L.bad = take(L.nblk * 4);
+  L.offsets = take(L.nblk * 4);
+  L.stat = take(16);
+  L.hc = take(L.Npad * D * esz);
+  L.yc = take(L.Npad * 4);
+  const size_t common_end = off;
+  // forward region
+  L.pm = take((int64_t)kMaxSplit * L.Npad * 4);
+  L.ps = take((int64_t)kMaxSplit * L.Npad * 4);
+  L.tgt = take(L.Npad * 4);
+  L.lrow = take(L.Npad * 4);
+  const size_t fwd_end = off;
+  // backward region overlays the forward region (the calls never overlap)
+  off = common_end;
+  L.mc = take(L.Npad * 4);
+  L.lsc = take(L.Npad * 4);
+  L.inv = take(std::max<int64_t>(N, 1) * 4);
+  L.G = take(L.Npad * L.Vc * esz);
+  L.slots = take((int64_t)kMaxDhSlots * L.Npad * D * 4);
+  L.dbp = take((L.Npad / bn) * L.Vpad * 4);
+  L.total = std::max(off, fwd_end);
+  return true;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+template <typename T> void set_lds_attr(const void* fn, int bytes) {
+  (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+}
+
+// Number of vocabulary splits for the forward grid: minimise
+// (waves of workgroups) x (tiles per split), ties to fewer splits.
+int choose_split(int n_rb, int n_vt) {
+  int best = 1;
+  int64_t best_cost = INT64_MAX;
+  for (int ns = 1; ns <= std::min(n_vt, kMaxSplit); ++ns) {
+    const int64_t waves = cdiv((int64_t)n_rb * ns, kCUs);
+    const int64_t cost = waves * cdiv(n_vt, ns);
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = ns;
+    }
+  }
+  return best;
+}
+
+lce_status_t zero_bytes(void* p, int64_t bytes, hipStream_t s) {
+  if (!p || bytes <= 0) return LCE_OK;
+  const int64_t n16 = bytes / 16;
+  const int tail = (int)(bytes - n16 * 16);
+  const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(cdiv(n16, 256), 4096));
+  LCE_LAUNCH("k_zero", k_zero, grid, 256, 0, s, (u32x4*)p, n16, (uint8_t*)p + n16 * 16, tail);
+  return LCE_OK;
+}
+
+lce_status_t fill_f32(float* p, int64_t n, float v, hipStream_t s) {
+  if (!p || n <= 0) return LCE_OK;
+  const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(cdiv(n, 256), 4096));
+  LCE_LAUNCH("k_fill_f32", k_fill_f32, grid, 256, 0, s, p, n, v);
+  return LCE_OK;
+}
+
+#define LCE_TRY(x)                       \
+  do {                                   \
+    lce_status_t st_ = (x);              \
+    if (st_ != LCE_OK) return st_;       \
+  } while (0)
+
+// ------------------------------------------------------------------ forward
+template <typename T>
+lce_status_t forward_impl(const T* H, const T* W, const T* b, const int64_t* labels,
+                          const int32_t* idx, int64_t C, int64_t N, int64_t D, int64_t V,
+                          float* loss, float* m, float* logs, float* row_loss, char* ws,
+                          const Layout& L, hipStream_t s) {
+  using Cf = Cfg<T>;
+  const int Cpad = (int)rup(C, 256);
+  T* Hc = reinterpret_cast<T*>(ws + L.hc);
+  int* yc = reinterpret_cast<int*>(ws + L.yc);
+  float* pm = reinterpret_cast<float*>(ws + L.pm);
+  float* ps = reinterpret_cast<float*>(ws + L.ps);
+  float* tgt = reinterpret_cast<float*>(ws + L.tgt);
+  float* lrow = reinterpret_cast<float*>(ws + L.lrow);
+
+  {
+    const int64_t vec = (int64_t)Cpad * (D / (16 / (int64_t)sizeof(T)));
+    const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(cdiv(vec, 256), 8192));
+    LCE_LAUNCH("k_gather", (k_gather<T>), grid, 256, 0, s, H, labels, idx, (int)C, Cpad, (int)D, Hc,
+               yc, (const float*)nullptr, (const float*)nullptr, (float*)nullptr, (float*)nullptr);
+  }
+  const int n_rb = Cpad / Cf::BN;
+  const int n_vt = (int)cdiv(V, Cf::BM);
+  const int n_split = choose_split(n_rb, n_vt);
+  const int n_work = n_rb * n_split;
+  const int per_xcd = (int)cdiv(n_work, 8);
+  set_lds_attr<T>((const void*)k_fwd<T>, Geo<T>::LDS_BYTES);
+  LCE_LAUNCH("k_fwd", (k_fwd<T>), per_xcd * 8, kThreads, Geo<T>::LDS_BYTES, s, W, b, Hc, yc, Cpad,
+             (int)D, (int)V, n_rb, n_split, n_vt, n_work, per_xcd, pm, ps, tgt);
+  LCE_TRY(fill_f32(m, N, -INFINITY, s));
+  LCE_TRY(fill_f32(logs, N, -INFINITY, s));
+  LCE_TRY(fill_f32(row_loss, N, 0.f, s));
+  LCE_LAUNCH("k_merge", k_merge, cdiv(C, 256), 256, 0, s, pm, ps, tgt, n_split, Cpad, (int)C, idx, m,
+             logs, row_loss, lrow);
+  LCE_LAUNCH("k_loss_sum", k_loss_sum, 1, 1024, 0, s, lrow, (int)C, loss);
+  return LCE_OK;
+}
+
+// ------------------------------------------------------------------ backward
+template <typename T>
+lce_status_t backward_impl(const T* H, const T* W, const T* b, const int64_t* labels,
+                           const int32_t* idx, int64_t C, int64_t N, int64_t D, int64_t V,
+                           const float* m, const float* logs, const float* grad_loss, T* dH, T* dW,
+                           T* db, char* ws, const Layout& L, hipStream_t s) {
+  using Cf = Cfg<T>;
+  const int Cpad = (int)rup(C, 256);
+  T* Hc = reinterpret_cast<T*>(ws + L.hc);
+  int* yc = reinterpret_cast<int*>(ws + L.yc);
+  float* mc = reinterpret_cast<float*>(ws + L.mc);
+  float* lsc = reinterpret_cast<float*>(ws + L.lsc);
+  int* inv = reinterpret_cast<int*>(ws + L.inv);
+  T* Gc = reinterpret_cast<T*>(ws + L.G);
+  float* slots = reinterpret_cast<float*>(ws + L.slots);
+  float* dbp = reinterpret_cast<float*>(ws + L.dbp);
+  const int64_t ldg = L.Vc;
+  const int64_t slot_stride = (int64_t)Cpad * D;
+  const int64_t lddb = L.Vpad;
+
+  {
+    const int64_t vec = (int64_t)Cpad * (D / (16 / (int64_t)sizeof(T)));
+    const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(cdiv(vec, 256), 8192));
+    LCE_LAUNCH("k_gather", (k_gather<T>), grid, 256, 0, s, H, labels, idx, (int)C, Cpad, (int)D, Hc,
+               yc, m, logs, mc, lsc);
+  }
+  {
+    const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(cdiv(N, 256), 4096));
+    LCE_LAUNCH("k_fill_i32", k_fill_i32, grid, 256, 0, s, inv, N, -1);
+    LCE_LAUNCH("k_inv_scatter", k_inv_scatter, cdiv(C, 256), 256, 0, s, idx, (int)C, inv);
+  }
+  const int n_rb = Cpad / Cf::BN;
+  const int n_nt = (int)cdiv(D, Cf::BN);
+  const int n_dh_mt = Cpad / Cf::BM;
+  set_lds_attr<T>((const void*)k_replay<T>, Geo<T>::LDS_BYTES);
+  set_lds_attr<T>((const void*)k_grad<T>, Geo<T>::LDS_BYTES);
+
+  int S = 0;  // dH k-splits, fixed by the first (widest) chunk
+  for (int64_t v0 = 0, chunk = 0; v0 < V; v0 += L.Vc, ++chunk) {
+    const int vc = (int)std::min<int64_t>(L.Vc, V - v0);
+    const int vtiles = (int)cdiv(vc, Cf::BM);
+    const int kpad = vtiles * Cf::BM;
+    // K4: replay this chunk into G.
+    {
+      const int n_work = n_rb * vtiles;
+      const int per_xcd = (int)cdiv(n_work, 8);
+      LCE_LAUNCH("k_replay", (k_replay<T>), per_xcd * 8, kThreads, Geo<T>::LDS_BYTES, s, W, b, Hc,
+                 yc, mc, lsc, Cpad, (int)D, (int)V, (int)v0, n_rb, n_work, per_xcd, Gc, ldg,
+                 db ? dbp : (float*)nullptr, lddb);
+    }
+    // K5: dH split so that one dH tile's K matches one dW tile's K (= Cpad).
+    if (chunk == 0) {
+      const double ratio = (double)kpad / (double)Cpad;
+      S = (int)std::max<int64_t>(1, std::min<int64_t>(kMaxDhSlots, (int64_t)(ratio + 0.5)));
+    }
+    int64_t ks_len = rup(cdiv(kpad, S), Cf::BK);
+    const int S_eff = (int)cdiv(kpad, ks_len);
+    const int n_dh = n_dh_mt * n_nt * S_eff;
+    const int n_dw = vtiles * n_nt;
+    LCE_LAUNCH("k_grad", (k_grad<T>), n_dh + n_dw, kThreads, Geo<T>::LDS_BYTES, s, Gc, ldg, kpad, Hc,
+               W, Cpad, (int)D, (int)v0, vc, (int)(V - v0), n_nt, n_dh_mt, (int)ks_len, n_dh, vtiles, slots,
+               slot_stride, chunk == 0 ? 0 : 1, dW, grad_loss, (int)C);
+  }
+  {
+    const int64_t vec = N * (D / 4);
+    const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(cdiv(vec, 256), 8192));
+    LCE_LAUNCH("k_dh_finalize", (k_dh_finalize<T>), grid, 256, 0, s, slots, S, slot_stride, inv, N,
+               (int)D, grad_loss, (int)C, dH);
+  }
+  if (db) {
+    const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(cdiv(V, 256), 4096));
+    LCE_LAUNCH("k_db_finalize", (k_db_finalize<T>), grid, 256, 0, s, dbp, n_rb, lddb, (int)V,
+               grad_loss, (int)C, db);
+  }
+  return LCE_OK;
+}
+
+bool dims_ok(int64_t N, int64_t D, int64_t V, lce_dtype_t dt) {
+  if (N < 0 || D <= 0 || V <= 0) return false;
+  if (dt != LCE_DTYPE_F32 && dt != LCE_DTYPE_BF16) return false;
+  return true;
+}
+
+lce_status_t shape_supported(int64_t N, int64_t D, int64_t V, lce_dtype_t dt) {
+  const int64_t vec = dt == LCE_DTYPE_BF16 ? 8 : 4;
+  if (D % vec != 0) return LCE_ERR_UNSUPPORTED;
+  if (N > (int64_t)1 << 30 || V > (int64_t)1 << 30 || D > (int64_t)1 << 20) return LCE_ERR_UNSUPPORTED;
+  if (N * D > ((int64_t)1 << 40) || V * D > ((int64_t)1 << 40)) return LCE_ERR_UNSUPPORTED;
+  return LCE_OK;
+}
+
+}  // namespace
+
+// ====================================================================== C ABI
+extern "C" {
+
+size_t lce_workspace_size(int64_t N, int64_t D, int64_t V, lce_dtype_t dt) {
+  Layout L;
+  if (!make_layout(N, D, V, dt, L)) return 0;
+  return L.total;
+}
+
+const char* lce_status_string(lce_status_t st) {
+  switch (st) {
+    case LCE_OK: return "ok";
+    case LCE_OK_EMPTY: return "ok: no supervised positions (C == 0); zero loss and gradients";
+    case LCE_ERR_ARG: return "invalid argument";
+    case LCE_ERR_LABEL: return "a supervised label lies outside [0, V)";
+    case LCE_ERR_WORKSPACE: return "workspace too small";
+    case LCE_ERR_HIP: return "HIP runtime error";
+    case LCE_ERR_UNSUPPORTED: return "unsupported shape";
+  }
+  return "unknown status";
+}
+
+lce_status_t lce_compact_valid(const int64_t* labels, const uint8_t* mask, int64_t N, int64_t V,
+                               int64_t ignore_index, int32_t* valid_idx, int64_t* C_host, void* ws,
+                               size_t ws_bytes, void* stream) {
+  try {
+    if (!C_host || N < 0 || V <= 0) return LCE_ERR_ARG;
+    if (N > 0 && (!labels || !valid_idx || !ws)) return LCE_ERR_ARG;
+    if (N > ((int64_t)1 << 30)) return LCE_ERR_UNSUPPORTED;
+    *C_host = 0;
+    if (N == 0) return LCE_OK_EMPTY;
+    const int64_t nblk = cdiv(N, kCmpBlock);
+    const size_t need = a256(nblk * 4) * 3 + 256;
+    if (ws_bytes < need || !aligned16(ws)) return LCE_ERR_WORKSPACE;
+    // Same offsets as the full layout (its compaction part depends on N only).
+    Layout L;
+    make_layout(N, 8, 1, LCE_DTYPE_BF16, L);
+    char* w = static_cast<char*>(ws);
+    int* counts = reinterpret_cast<int*>(w + L.counts);
+    int* bad = reinterpret_cast<int*>(w + L.bad);
+    int* offsets = reinterpret_cast<int*>(w + L.offsets);
+    int* stat = reinterpret_cast<int*>(w + L.stat);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    LCE_LAUNCH("k_cmp_count", k_cmp_count, nblk, kCmpBlock, 0, s, labels, mask, N, V, ignore_index,
+               counts, bad);
+    LCE_LAUNCH("k_cmp_scan", k_cmp_scan, 1, 1024, 0, s, counts, bad, (int)nblk, offsets, stat);
+    LCE_LAUNCH("k_cmp_scatter", k_cmp_scatter, nblk, kCmpBlock, 0, s, labels, mask, N, ignore_index,
+               offsets, valid_idx);
+    int host_stat[2] = {0, 0};
+    if (hipMemcpyAsync(host_stat, stat, sizeof(host_stat), hipMemcpyDeviceToHost, s) != hipSuccess)
+      return LCE_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return LCE_ERR_HIP;
+    if (host_stat[1]) return LCE_ERR_LABEL;
+    *C_host = host_stat[0];
+    return host_stat[0] > 0 ? LCE_OK : LCE_OK_EMPTY;
+  } catch (...) {
+    return LCE_ERR_HIP;
+  }
+}
+
+lce_status_t lce_forward(const void* H, const void* W, const void* b, const int64_t* labels,
+                         const int32_t* valid_idx, int64_t C, int64_t N, int64_t D, int64_t V,
+                         lce_dtype_t dt, float* loss, float* m, float* logs, float* row_loss,
+                         void* ws, size_t ws_bytes, void* stream) {
+  try {
+    if (!dims_ok(N, D, V, dt) || C < 0 || C > N) return LCE_ERR_ARG;
+    if (!loss || (N > 0 && (!m || !logs))) return LCE_ERR_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (C == 0) {
+      LCE_LAUNCH("k_store_scalar", k_store_scalar, 1, 1, 0, s, loss, 0.f);
+      LCE_TRY(fill_f32(m, N, -INFINITY, s));
+      LCE_TRY(fill_f32(logs, N, -INFINITY, s));
+      LCE_TRY(fill_f32(row_loss, N, 0.f, s));
+      return LCE_OK_EMPTY;
+    }
+    if (!H || !W || !labels || !valid_idx || !ws) return LCE_ERR_ARG;
+    if (!aligned16(H) || !aligned16(W) || !aligned16(ws)) return LCE_ERR_ARG;
+    LCE_TRY(shape_supported(N, D, V, dt));
+    Layout L;
+    if (!make_layout(N, D, V, dt, L)) return LCE_ERR_ARG;
+    if (ws_bytes < L.total) return LCE_ERR_WORKSPACE;
+    char* w = static_cast<char*>(ws);
+    if (dt == LCE_DTYPE_BF16)
+      return forward_impl<uint16_t>((const uint16_t*)H, (const uint16_t*)W, (const uint16_t*)b, labels,
+                                    valid_idx, C, N, D, V, loss, m, logs, row_loss, w, L, s);
+    return forward_impl<float>((const float*)H, (const float*)W, (const float*)b, labels, valid_idx, C,
+                               N, D, V, loss, m, logs, row_loss, w, L, s);
+  } catch (...) {
+    return LCE_ERR_HIP;
+  }
+}
+
+lce_status_t lce_backward(const void* H, const void* W, const void* b, const int64_t* labels,
+                          const int32_t* valid_idx, int64_t C, int64_t N, int64_t D, int64_t V,
+                          lce_dtype_t dt, const float* m, const float* logs, const float* grad_loss,
+                          void* dH, void* dW, void* db, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    if (!dims_ok(N, D, V, dt) || C < 0 || C > N) return LCE_ERR_ARG;
+    if (!dW || (N > 0 && !dH)) return LCE_ERR_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t esz = dt == LCE_DTYPE_BF16 ? 2 : 4;
+    if (C == 0) {
+      LCE_TRY(zero_bytes(dH, N * D * esz, s));
+      LCE_TRY(zero_bytes(dW, V * D * esz, s));
+      LCE_TRY(zero_bytes(db, V * esz, s));
+      return LCE_OK_EMPTY;
+    }
+    if (!H || !W || !labels || !valid_idx || !m || !logs || !ws) return LCE_ERR_ARG;
+    if (!aligned16(H) || !aligned16(W) || !aligned16(ws) || !aligned16(dH) || !aligned16(dW))
+      return LCE_ERR_ARG;
+    LCE_TRY(shape_supported(N, D, V, dt));
+    Layout L;
+    if (!make_layout(N, D, V, dt, L)) return LCE_ERR_ARG;
+    if (ws_bytes < L.total) return LCE_ERR_WORKSPACE;
+    char* w = static_cast<char*>(ws);
+    if (dt == LCE_DTYPE_BF16)
+      return backward_impl<uint16_t>((const uint16_t*)H, (const uint16_t*)W, (const uint16_t*)b, labels,
+                                     valid_idx, C, N, D, V, m, logs, grad_loss, (uint16_t*)dH,
+                                     (uint16_t*)dW, (uint16_t*)db, w, L, s);
+    return backward_impl<float>((const float*)H, (const float*)W, (const float*)b, labels, valid_idx, C,
+                                N, D, V, m, logs, grad_loss, (float*)dH, (float*)dW, (float*)db, w, L,
+                                s);
+  } catch (...) {
+    return LCE_ERR_HIP;
+  }
+}
+
+lce_status_t lce_profile_start(int32_t max_launches) {
+  try {
+    Prof& p = g_prof;
+    if (max_launches <= 0) return LCE_ERR_ARG;
+    if ((int)p.ev.size() < 2 * max_launches) {
+      for (hipEvent_t e : p.ev) (void)hipEventDestroy(e);
+      p.ev.assign(2 * (size_t)max_launches, nullptr);
+      for (auto& e : p.ev)
+        if (hipEventCreate(&e) != hipSuccess) return LCE_ERR_HIP;
+    }
+    p.kid.assign((size_t)max_launches, -1);
+    p.max = max_launches;
+    p.used = 0;
+    p.names.clear();
+    p.ms.clear();
+    p.cnt.clear();
+    p.on = true;
+    return LCE_OK;
+  } catch (...) {
+    return LCE_ERR_HIP;
+  }
+}
+
+lce_status_t lce_profile_stop(void) {
+  Prof& p = g_prof;
+  p.on = false;
+  for (int i = 0; i < p.used; ++i) {
+    float ms = 0.f;
+    if (hipEventSynchronize(p.ev[2 * i + 1]) != hipSuccess) return LCE_ERR_HIP;
+    if (hipEventElapsedTime(&ms, p.ev[2 * i], p.ev[2 * i + 1]) != hipSuccess) return LCE_ERR_HIP;
+    p.ms[p.kid[i]] += ms;
+    p.cnt[p.kid[i]] += 1;
+  }
+  p.used = 0;
+  return LCE_OK;
+}
+
+int32_t lce_profile_count(void) { return (int32_t)g_prof.names.size(); }
+
+lce_status_t lce_profile_entry(int32_t i, char* name, int32_t name_cap, double* total_ms,
+                               int64_t* launches) {
+  Prof& p = g_prof;
+  if (i < 0 || i >= (int32_t)p.names.size()) return LCE_ERR_ARG;
+  if (name && name_cap > 0) {
+    std::strncpy(name, p.names[i].c_str(), (size_t)name_cap - 1);
+    name[name_cap - 1] = 0;
+  }
+  if (total_ms) *total_ms = p.ms[i];
+  if (launches) *launches = p.cnt[i];
+  return LCE_OK;
+}
+
+}  // extern "C"

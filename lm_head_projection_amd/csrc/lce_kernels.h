@@ -1,0 +1,614 @@
+// Kernels of the fused linear-cross-entropy path (gfx950).
+//
+//   K0  k_cmp_count / k_cmp_scan / k_cmp_scatter   valid-token compaction
+//   K1  k_gather                                   supervised rows H[idx] -> Hc
+//   K2  k_fwd                                      score tiles + running (m, s)
+//   K3  k_merge / k_loss_sum                       split merge, per-row CE, mean
+//   K4  k_replay                                   score tiles -> G = p - onehot
+//   K5  k_grad                                     dH (+= G W) and dW (= G^T Hc)
+//   K6  k_dh_finalize / k_db_finalize              ordered sums, lambda/C, cast
+//
+// Page references are to "分块交叉熵：从输出投影开始省保存量" (glenzli.com):
+// section 01 (objective, tile steps), section 02 (running LSE), section 04
+// (replay and the three gradient accumulations).
+#pragma once
+
+#include "lce_device.h"
+
+namespace lce {
+
+// ============================================================== K0 compaction
+// a_i = 1[mask_i] 1[y_i != ignore] (section 01).  Three passes: per-block
+// counts, one-block exclusive scan of the counts, ordered scatter.  No atomics.
+constexpr int kCmpBlock = 256;
+
+__device__ __forceinline__ bool is_supervised(const int64_t* labels, const uint8_t* mask, int64_t i,
+                                              int64_t ignore) {
+  return labels[i] != ignore && (mask == nullptr || mask[i] != 0);
+}
+
+__global__ __launch_bounds__(kCmpBlock) void k_cmp_count(const int64_t* __restrict__ labels,
+                                                         const uint8_t* __restrict__ mask, int64_t N,
+                                                         int64_t V, int64_t ignore, int* counts,
+                                                         int* bad) {
+  __shared__ int s_cnt[kCmpBlock / kWarp];
+  __shared__ int s_bad[kCmpBlock / kWarp];
+  const int64_t i = (int64_t)blockIdx.x * kCmpBlock + threadIdx.x;
+  bool sup = false, oob = false;
+  if (i < N) {
+    sup = is_supervised(labels, mask, i, ignore);
+    const int64_t y = labels[i];
+    oob = sup && (y < 0 || y >= V);
+  }
+  const uint64_t bal = __ballot(sup);
+  const int anybad = __any(oob);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) {
+    s_cnt[wave] = __popcll(bal);
+    s_bad[wave] = anybad;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int c = 0, b = 0;
+    for (int w = 0; w < kCmpBlock / kWarp; ++w) {
+      c += s_cnt[w];
+      b |= s_bad[w];
+    }
+    counts[blockIdx.x] = c;
+    bad[blockIdx.x] = b;
+  }
+}
+
+// Block-wide exclusive scan helper for 1024 threads.
+__device__ __forceinline__ int block_excl_scan_1024(int v, int* s_w, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) s_w[wave] = x;
+  __syncthreads();
+  if (wave == 0) {
+    int w = lane < 16 ? s_w[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      const int y = __shfl_up(w, off);
+      if (lane >= off) w += y;
+    }
+    if (lane < 16) s_w[lane] = w;
+  }
+  __syncthreads();
+  const int excl = x - v + (wave > 0 ? s_w[wave - 1] : 0);
+  total = s_w[15];
+  __syncthreads();
+  return excl;
+}
+
+// stat[0] = C, stat[1] = 1 if any supervised label is out of range.
+__global__ __launch_bounds__(1024) void k_cmp_scan(const int* __restrict__ counts,
+                                                   const int* __restrict__ bad, int nblk,
+                                                   int* offsets, int* stat) {
+  __shared__ int s_w[16];
+  int carry = 0, anybad = 0;
+  for (int base = 0; base < nblk; base += 1024) {
+    const int j = base + threadIdx.x;
+    const int v = j < nblk ? counts[j] : 0;
+    const int b = j < nblk ? bad[j] : 0;
+    int total;
+    const int excl = block_excl_scan_1024(v, s_w, total);
+    if (j < nblk) offsets[j] = carry + excl;
+    carry += total;
+    anybad |= __syncthreads_or(b);
+  }
+  if (threadIdx.x == 0) {
+    stat[0] = carry;
+    stat[1] = anybad;
+  }
+}
+
+__global__ __launch_bounds__(kCmpBlock) void k_cmp_scatter(const int64_t* __restrict__ labels,
+                                                           const uint8_t* __restrict__ mask,
+                                                           int64_t N, int64_t ignore,
+                                                           const int* __restrict__ offsets,
+                                                           int32_t* __restrict__ idx) {
+  __shared__ int s_cnt[kCmpBlock / kWarp];
+  const int64_t i = (int64_t)blockIdx.x * kCmpBlock + threadIdx.x;
+  const bool sup = i < N && is_supervised(labels, mask, i, ignore);
+  const uint64_t bal = __ballot(sup);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) s_cnt[wave] = __popcll(bal);
+  __syncthreads();
+  int off = offsets[blockIdx.x];
+  for (int w = 0; w < wave; ++w) off += s_cnt[w];
+  const uint64_t below = lane == 0 ? 0ull : (bal & ((~0ull) >> (64 - lane)));
+  if (sup) idx[off + __popcll(below)] = (int32_t)i;
+}
+
+// ============================================================== K1 gather
+// Hc[c] = H[idx[c]] for c < C, 0 for C <= c < Cpad; yc[c] = y[idx[c]] (-1 for
+// padding).  With m/logs given (backward), mc/lsc hold them per compact row;
+// padding rows get m = +inf so their replayed p is 0.
+template <typename T>
+__global__ __launch_bounds__(256) void k_gather(const T* __restrict__ H,
+                                                const int64_t* __restrict__ labels,
+                                                const int32_t* __restrict__ idx, int C, int Cpad,
+                                                int D, T* __restrict__ Hc, int* __restrict__ yc,
+                                                const float* __restrict__ m,
+                                                const float* __restrict__ logs, float* mc,
+                                                float* lsc) {
+  constexpr int VEC = 16 / sizeof(T);
+  const int vpr = D / VEC;
+  const int64_t total = (int64_t)Cpad * vpr;
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total;
+       q += (int64_t)gridDim.x * blockDim.x) {
+    const int c = (int)(q / vpr), kv = (int)(q % vpr);
+    u32x4 v = u32x4{0u, 0u, 0u, 0u};
+    int src = -1;
+    if (c < C) {
+      src = idx[c];
+      v = *reinterpret_cast<const u32x4*>(H + (int64_t)src * D + kv * VEC);
+    }
+    *reinterpret_cast<u32x4*>(Hc + (int64_t)c * D + kv * VEC) = v;
+    if (kv == 0) {
+      yc[c] = c < C ? (int)labels[src] : -1;
+      if (mc) {
+        mc[c] = c < C ? m[src] : INFINITY;
+        lsc[c] = c < C ? logs[src] : 0.f;
+      }
+    }
+  }
+}
+
+// ============================================================== K2 forward
+// Work item = (row block rb, vocabulary split).  The workgroup walks the
+// split's vocabulary tiles in order; for each tile it forms the score tile
+// Z^T = W_B . Hc_T^T (+ b) with MFMA (FORWARD/PROJECT, section 01), then
+// updates each row's running max and exp-sum (REDUCE/CAPTURE, section 02
+// recurrence) and captures Z_{i,y_i} from the tile holding y_i by global
+// column id.  The vocabulary is the MFMA M axis, so a lane's 64 scores of a
+// row lie in its own registers and the tile needs no cross-lane reduction;
+// lanes merge once per split.  Output: partial (m, s) per (split, row).
+// Adds b_v to every score of the tile after the K loop (one rounding, so a
+// large bias does not coarsen the fp32 partial sums of H.W).
+template <typename T>
+__device__ __forceinline__ void add_bias(f32x16_t (&acc)[Geo<T>::TM][Geo<T>::TN],
+                                         const T* __restrict__ bias, int vbase, int V, int lane) {
+  using G = Geo<T>;
+#pragma unroll
+  for (int tm = 0; tm < G::TM; ++tm)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int v = vbase + tm * 32 + 8 * i4 + 4 * (lane >> 5);
+      float bv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) bv[r] = (v + r < V) ? to_f32(bias[v + r]) : 0.f;
+#pragma unroll
+      for (int tn = 0; tn < G::TN; ++tn)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[tm][tn][i4 * 4 + r] += bv[r];
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_fwd(const T* __restrict__ W, const T* __restrict__ bias,
+                                                  const T* __restrict__ Hc,
+                                                  const int* __restrict__ yc, int Cpad, int D, int V,
+                                                  int n_rb, int n_split, int n_vt, int n_work,
+                                                  int per_xcd, float* __restrict__ pm,
+                                                  float* __restrict__ ps, float* __restrict__ tgt) {
+  using C = Cfg<T>;
+  using G = Geo<T>;
+  extern __shared__ __align__(16) char smem_raw[];
+  T* smem = reinterpret_cast<T*>(smem_raw);
+  const int w = xcd_remap(blockIdx.x, per_xcd);
+  if (w >= n_work) return;
+  const int rb = w % n_rb, split = w / n_rb;
+  const int t0 = (int)((int64_t)split * n_vt / n_split);
+  const int t1 = (int)((int64_t)(split + 1) * n_vt / n_split);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave % G::WGM, wn = wave / G::WGM;
+  const int n0 = rb * C::BN;
+
+  int row[G::TN], y[G::TN];
+  float mrun[G::TN], srun[G::TN];
+#pragma unroll
+  for (int tn = 0; tn < G::TN; ++tn) {
+    row[tn] = n0 + wn * G::WTN + tn * 32 + (lane & 31);
+    y[tn] = yc[row[tn]];
+    mrun[tn] = -INFINITY;
+    srun[tn] = 0.f;
+  }
+  const int nsteps = (D + C::BK - 1) / C::BK;
+
+  for (int t = t0; t < t1; ++t) {
+    const int m0 = t * C::BM;
+    const int vbase = m0 + wm * G::WTM;
+    f32x16_t acc[G::TM][G::TN];
+    zero_acc<T>(acc);
+    gemm_tile<T, true, true>(W, (int64_t)V * D, D, m0, Hc, (int64_t)Cpad * D, D, n0, 0, D, nsteps,
+                           acc, smem);
+    if (bias) add_bias<T>(acc, bias, vbase, V, lane);
+
+    if (m0 + C::BM > V) {  // ragged last tile: columns past V do not exist
+#pragma unroll
+      for (int tm = 0; tm < G::TM; ++tm)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (vbase + acc_row(tm, i, lane) >= V)
+#pragma unroll
+            for (int tn = 0; tn < G::TN; ++tn) acc[tm][tn][i] = -INFINITY;
+    }
+#pragma unroll
+    for (int tn = 0; tn < G::TN; ++tn) {
+      float mloc = -INFINITY;
+#pragma unroll
+      for (int tm = 0; tm < G::TM; ++tm)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, acc[tm][tn][i]);
+      const float mnew = fmaxf(mrun[tn], mloc);
+      const float mref = (mnew == -INFINITY) ? 0.f : mnew;
+      float ssum = 0.f;
+      if constexpr (sizeof(T) == 4) {
+        // fp32: Z - m is exact for nearby values, so a large common shift
+        // costs no precision (section 02: compute relative to m).
+#pragma unroll
+        for (int tm = 0; tm < G::TM; ++tm)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) ssum += __builtin_amdgcn_exp2f((acc[tm][tn][i] - mref) * kLog2e);
+      } else {
+        const float mneg = -mref * kLog2e;
+#pragma unroll
+        for (int tm = 0; tm < G::TM; ++tm)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) ssum += __builtin_amdgcn_exp2f(fmaf(acc[tm][tn][i], kLog2e, mneg));
+      }
+      // First tile: the rescale factor of the (empty) old sum is 0.
+      const float alpha = (mnew == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f((mrun[tn] - mnew) * kLog2e);
+      srun[tn] = srun[tn] * alpha + ssum;
+      mrun[tn] = mnew;
+      // Target capture by global column id.
+      const int d = y[tn] - vbase;
+      if ((unsigned)d < (unsigned)G::WTM) {
+#pragma unroll
+        for (int tm = 0; tm < G::TM; ++tm)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (acc_row(tm, i, lane) == d) tgt[row[tn]] = acc[tm][tn][i];
+      }
+    }
+  }
+
+  // Lanes l and l^32 hold the same rows (different vocabulary entries).
+#pragma unroll
+  for (int tn = 0; tn < G::TN; ++tn) {
+    const float mo = __shfl_xor(mrun[tn], 32);
+    const float so = __shfl_xor(srun[tn], 32);
+    lse_merge(mrun[tn], srun[tn], mo, so);
+  }
+  // Waves with the same wn and different wm hold the same rows.
+  float* red = reinterpret_cast<float*>(smem_raw);  // LDS is free: gemm_tile ends on a barrier
+  static_assert(G::WGM == 2, "merge below assumes two waves per row range");
+  if (wm == 1 && lane < 32) {
+#pragma unroll
+    for (int tn = 0; tn < G::TN; ++tn) {
+      red[((wn * G::TN + tn) * 32 + lane) * 2 + 0] = mrun[tn];
+      red[((wn * G::TN + tn) * 32 + lane) * 2 + 1] = srun[tn];
+    }
+  }
+  __syncthreads();
+  if (wm == 0 && lane < 32) {
+#pragma unroll
+    for (int tn = 0; tn < G::TN; ++tn) {
+      const float mo = red[((wn * G::TN + tn) * 32 + lane) * 2 + 0];
+      const float so = red[((wn * G::TN + tn) * 32 + lane) * 2 + 1];
+      lse_merge(mrun[tn], srun[tn], mo, so);
+      pm[(int64_t)split * Cpad + row[tn]] = mrun[tn];
+      ps[(int64_t)split * Cpad + row[tn]] = srun[tn];
+    }
+  }
+}
+
+// ============================================================== K3 merge + loss
+// Per supervised row: merge the split partials in split order (online-softmax
+// merge), log s, l_i = (m - Z_{i,y_i}) + log s (section 02), scatter m, log s
+// (and the row CE) to the row's position.
+__global__ __launch_bounds__(256) void k_merge(const float* __restrict__ pm, const float* __restrict__ ps,
+                                               const float* __restrict__ tgt, int n_split, int Cpad,
+                                               int C, const int32_t* __restrict__ idx,
+                                               float* __restrict__ m_out, float* __restrict__ logs_out,
+                                               float* __restrict__ row_loss, float* __restrict__ lrow) {
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= C) return;
+  float m = -INFINITY, s = 0.f;
+  for (int k = 0; k < n_split; ++k) lse_merge(m, s, pm[(int64_t)k * Cpad + c], ps[(int64_t)k * Cpad + c]);
+  const float ls = logf(s);
+  const float l = (m - tgt[c]) + ls;
+  const int n = idx[c];
+  m_out[n] = m;
+  logs_out[n] = ls;
+  if (row_loss) row_loss[n] = l;
+  lrow[c] = l;
+}
+
+// loss = (1/C) sum_c l_c, summed in float64 in a fixed order.
+__global__ __launch_bounds__(1024) void k_loss_sum(const float* __restrict__ lrow, int C,
+                                                   float* __restrict__ loss) {
+  __shared__ double s[1024];
+  double acc = 0.0;
+  for (int c = threadIdx.x; c < C; c += 1024) acc += (double)lrow[c];
+  s[threadIdx.x] = acc;
+  __syncthreads();
+  for (int off = 512; off > 0; off >>= 1) {
+    if (threadIdx.x < off) s[threadIdx.x] += s[threadIdx.x + off];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) loss[0] = (float)(s[0] / (double)C);
+}
+
+__global__ void k_fill_f32(float* __restrict__ p, int64_t n, float v) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+__global__ void k_fill_i32(int* __restrict__ p, int64_t n, int v) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+// Zero n16 16-byte words (plus a byte tail).
+__global__ void k_zero(u32x4* __restrict__ p, int64_t n16, uint8_t* __restrict__ tail, int ntail) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = u32x4{0u, 0u, 0u, 0u};
+  if (blockIdx.x == 0 && (int)threadIdx.x < ntail) tail[threadIdx.x] = 0;
+}
+__global__ void k_inv_scatter(const int32_t* __restrict__ idx, int C, int* __restrict__ inv) {
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c < C) inv[idx[c]] = c;
+}
+__global__ void k_store_scalar(float* __restrict__ p, float v) { p[0] = v; }
+
+// ============================================================== K4 replay
+// One (row block, vocabulary tile) per workgroup: recompute the score tile,
+// p = exp((Z - m) - log s) from the saved statistics, subtract 1 at the target
+// column (global id), write G = p - onehot (unscaled; lambda/C is applied in
+// the gradient epilogues) into the chunk buffer G[c][v - v0], and, with a
+// bias, the per-row-block column sums of G (db partials) in a fixed order.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_replay(
+    const T* __restrict__ W, const T* __restrict__ bias, const T* __restrict__ Hc,
+    const int* __restrict__ yc, const float* __restrict__ mc, const float* __restrict__ lsc, int Cpad,
+    int D, int V, int v0, int n_rb, int n_work, int per_xcd, T* __restrict__ Gc, int64_t ldg,
+    float* __restrict__ dbp, int64_t lddb) {
+  using C = Cfg<T>;
+  using G = Geo<T>;
+  extern __shared__ __align__(16) char smem_raw[];
+  T* smem = reinterpret_cast<T*>(smem_raw);
+  const int w = xcd_remap(blockIdx.x, per_xcd);
+  if (w >= n_work) return;
+  const int rb = w % n_rb, vt = w / n_rb;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave % G::WGM, wn = wave / G::WGM;
+  const int n0 = rb * C::BN;
+  const int m0 = v0 + vt * C::BM;
+  const int vbase = m0 + wm * G::WTM;
+
+  f32x16_t acc[G::TM][G::TN];
+  zero_acc<T>(acc);
+  const int nsteps = (D + C::BK - 1) / C::BK;
+  gemm_tile<T, true, true>(W, (int64_t)V * D, D, m0, Hc, (int64_t)Cpad * D, D, n0, 0, D, nsteps,
+                           acc, smem);
+  if (bias) add_bias<T>(acc, bias, vbase, V, lane);
+
+#pragma unroll
+  for (int tn = 0; tn < G::TN; ++tn) {
+    const int r = n0 + wn * G::WTN + tn * 32 + (lane & 31);
+    // p = exp((Z - m) - log s) from the saved statistics (section 04).
+    const float mr = mc[r], lr = lsc[r];
+    if constexpr (sizeof(T) == 4) {
+#pragma unroll
+      for (int tm = 0; tm < G::TM; ++tm)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          acc[tm][tn][i] = __builtin_amdgcn_exp2f(((acc[tm][tn][i] - mr) - lr) * kLog2e);
+    } else {
+      const float ml = mr * kLog2e, ll = lr * kLog2e;
+#pragma unroll
+      for (int tm = 0; tm < G::TM; ++tm)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          acc[tm][tn][i] = __builtin_amdgcn_exp2f(fmaf(acc[tm][tn][i], kLog2e, -ml) - ll);
+    }
+    const int d = yc[r] - vbase;
+    if ((unsigned)d < (unsigned)G::WTM) {
+#pragma unroll
+      for (int tm = 0; tm < G::TM; ++tm)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (acc_row(tm, i, lane) == d) acc[tm][tn][i] -= 1.f;
+    }
+  }
+  if (m0 + C::BM > V) {
+#pragma unroll
+    for (int tm = 0; tm < G::TM; ++tm)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (vbase + acc_row(tm, i, lane) >= V)
+#pragma unroll
+          for (int tn = 0; tn < G::TN; ++tn) acc[tm][tn][i] = 0.f;
+  }
+  // Store G (4 consecutive vocabulary entries of one row per lane and group).
+#pragma unroll
+  for (int tn = 0; tn < G::TN; ++tn) {
+    const int r = n0 + wn * G::WTN + tn * 32 + (lane & 31);
+    T* grow = Gc + (int64_t)r * ldg + (vbase - v0);
+#pragma unroll
+    for (int tm = 0; tm < G::TM; ++tm)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int off = tm * 32 + 8 * i4 + 4 * (lane >> 5);
+        if constexpr (sizeof(T) == 2) {
+          const uint32_t lo = (uint32_t)from_f32<uint16_t>(acc[tm][tn][i4 * 4 + 0]) |
+                              ((uint32_t)from_f32<uint16_t>(acc[tm][tn][i4 * 4 + 1]) << 16);
+          const uint32_t hi = (uint32_t)from_f32<uint16_t>(acc[tm][tn][i4 * 4 + 2]) |
+                              ((uint32_t)from_f32<uint16_t>(acc[tm][tn][i4 * 4 + 3]) << 16);
+          *reinterpret_cast<u32x2*>(grow + off) = u32x2{lo, hi};
+        } else {
+          *reinterpret_cast<f32x4_t*>(grow + off) =
+              f32x4_t{acc[tm][tn][i4 * 4 + 0], acc[tm][tn][i4 * 4 + 1], acc[tm][tn][i4 * 4 + 2],
+                      acc[tm][tn][i4 * 4 + 3]};
+        }
+      }
+  }
+  if (dbp == nullptr) return;
+  // Column sums over this workgroup's rows: first the TN rows a lane holds,
+  // then the 32 lanes of the half-wave (butterfly), then the WGN waves.
+  constexpr int NV = G::TM * 16;
+  float cs[NV];
+#pragma unroll
+  for (int tm = 0; tm < G::TM; ++tm)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float s = 0.f;
+#pragma unroll
+      for (int tn = 0; tn < G::TN; ++tn) s += acc[tm][tn][i];
+      cs[tm * 16 + i] = s;
+    }
+  halfwave_reduce_scatter<NV>(cs, lane);
+  constexpr int PER = NV / 32;
+  float* red = reinterpret_cast<float*>(smem_raw);  // free after gemm_tile's final barrier
+  // red[wn][wm][lane][PER]
+#pragma unroll
+  for (int j = 0; j < PER; ++j) red[((wn * G::WGM + wm) * 64 + lane) * PER + j] = cs[j];
+  __syncthreads();
+  if (wn == 0) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      float s = red[((0 * G::WGM + wm) * 64 + lane) * PER + j];
+#pragma unroll
+      for (int q = 1; q < G::WGN; ++q) s += red[((q * G::WGM + wm) * 64 + lane) * PER + j];
+      const int e = (lane & 31) * PER + j;
+      const int v = vbase + acc_row(e >> 4, e & 15, lane);
+      if (v < V) dbp[(int64_t)rb * lddb + v] = s;
+    }
+  }
+}
+
+
+// ============================================================== K5 gradients
+// One launch per vocabulary chunk, two kinds of output tiles:
+//  * dH tiles (first n_dh blocks): slot[ks][c][d] (+)= sum_{v in split ks}
+//    G[c][v] W[v0+v][d]  (dH_T += G_{T,B} W_B, section 04).  The chunk's
+//    vocabulary range is cut into S splits; slot ks accumulates split ks of
+//    every chunk in chunk order (stream order), so the sum is deterministic.
+//  * dW tiles: dW[v0+v][d] = (lambda/C) sum_c G[c][v] Hc[c][d]
+//    (dW_B += G^T H_T summed over every row block inside one tile, so each dW
+//    row is written exactly once).
+// Operands: G is K-contiguous for dH (k = v) and K-outer for dW (k = c); W
+// (k = v) and Hc (k = c) are K-outer; the loaders transpose them in registers.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_grad(
+    const T* __restrict__ Gc, int64_t ldg, int kpad_g, const T* __restrict__ Hc,
+    const T* __restrict__ W, int Cpad, int D, int v0, int vc, int w_rows, int n_nt, int n_dh_mt, int ks_len,
+    int n_dh, int n_dw_mt, float* __restrict__ slots, int64_t slot_stride, int accumulate,
+    T* __restrict__ dW, const float* __restrict__ grad_loss, int Ctrue) {
+  using C = Cfg<T>;
+  using G = Geo<T>;
+  extern __shared__ __align__(16) char smem_raw[];
+  T* smem = reinterpret_cast<T*>(smem_raw);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave % G::WGM, wn = wave / G::WGM;
+  f32x16_t acc[G::TM][G::TN];
+  zero_acc<T>(acc);
+  const int b = blockIdx.x;
+  if (b < n_dh) {
+    const int mt = b % n_dh_mt;
+    const int q = b / n_dh_mt;
+    const int nt = q % n_nt, ks = q / n_nt;
+    const int m0 = mt * C::BM, n0 = nt * C::BN;
+    const int kb = ks * ks_len;
+    const int ke_a = min(kb + ks_len, kpad_g);
+    const int nsteps = (ke_a - kb + C::BK - 1) / C::BK;
+    if (nsteps > 0)
+      gemm_tile<T, true, false>(Gc, (int64_t)Cpad * ldg, ldg, m0, W + (int64_t)v0 * D,
+                                (int64_t)w_rows * D, D, n0, kb, ke_a, nsteps, acc, smem);
+    float* slot = slots + (int64_t)ks * slot_stride;
+#pragma unroll
+    for (int tn = 0; tn < G::TN; ++tn) {
+      const int n = n0 + wn * G::WTN + tn * 32 + (lane & 31);
+      if (n >= D) continue;
+#pragma unroll
+      for (int tm = 0; tm < G::TM; ++tm)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = m0 + wm * G::WTM + acc_row(tm, i, lane);
+          float* p = slot + (int64_t)r * D + n;
+          *p = accumulate ? (*p + acc[tm][tn][i]) : acc[tm][tn][i];
+        }
+    }
+  } else {
+    const int q = b - n_dh;
+    const int mt = q % n_dw_mt, nt = q / n_dw_mt;
+    const int m0 = mt * C::BM, n0 = nt * C::BN;
+    const int nsteps = Cpad / C::BK;
+    gemm_tile<T, false, false>(Gc, (int64_t)Cpad * ldg, ldg, m0, Hc, (int64_t)Cpad * D, D, n0, 0, Cpad,
+                               nsteps, acc, smem);
+    const float scale = (grad_loss ? grad_loss[0] : 1.f) / (float)Ctrue;
+#pragma unroll
+    for (int tn = 0; tn < G::TN; ++tn) {
+      const int n = n0 + wn * G::WTN + tn * 32 + (lane & 31);
+      if (n >= D) continue;
+#pragma unroll
+      for (int tm = 0; tm < G::TM; ++tm)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = m0 + wm * G::WTM + acc_row(tm, i, lane);
+          if (r < vc) dW[(int64_t)(v0 + r) * D + n] = from_f32<T>(scale * acc[tm][tn][i]);
+        }
+    }
+  }
+}
+
+// ============================================================== K6 finalize
+// dH[n] = (lambda/C) sum_ks slot[ks][inv[n]] for supervised rows, 0 otherwise.
+template <typename T>
+__global__ void k_dh_finalize(const float* __restrict__ slots, int S, int64_t slot_stride,
+                              const int* __restrict__ inv, int64_t N, int D,
+                              const float* __restrict__ grad_loss, int Ctrue, T* __restrict__ dH) {
+  const float scale = (grad_loss ? grad_loss[0] : 1.f) / (float)Ctrue;
+  const int vpr = D / 4;
+  const int64_t total = N * vpr;
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total;
+       q += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t n = q / vpr;
+    const int d = (int)(q % vpr) * 4;
+    const int c = inv[n];
+    float o[4] = {0.f, 0.f, 0.f, 0.f};
+    if (c >= 0) {
+      for (int s = 0; s < S; ++s) {
+        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(slots + s * slot_stride + (int64_t)c * D + d);
+        o[0] += v[0];
+        o[1] += v[1];
+        o[2] += v[2];
+        o[3] += v[3];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j] *= scale;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dH[n * D + d + j] = from_f32<T>(o[j]);
+  }
+}
+
+// db[v] = (lambda/C) sum_rb dbp[rb][v] in row-block order.
+template <typename T>
+__global__ void k_db_finalize(const float* __restrict__ dbp, int n_rb, int64_t lddb, int V,
+                              const float* __restrict__ grad_loss, int Ctrue, T* __restrict__ db) {
+  const float scale = (grad_loss ? grad_loss[0] : 1.f) / (float)Ctrue;
+  for (int v = blockIdx.x * blockDim.x + threadIdx.x; v < V; v += gridDim.x * blockDim.x) {
+    float s = 0.f;
+    for (int rb = 0; rb < n_rb; ++rb) s += dbp[(int64_t)rb * lddb + v];
+    db[v] = from_f32<T>(scale * s);
+  }
+}
+
+}  // namespace lce

@@ -1,0 +1,111 @@
+"""Shared helpers for the GPU tests: run the HIP path through the C ABI on a
+workload and compare with the oracle at the stated tolerances.
+
+Tolerances (derived from the arithmetic and the target bar):
+  bf16 inputs: loss |L - L*| <= 1e-3 |L*|; m, log s: |x - x*| <= 1e-3 max(1, |x*|);
+               dH, dW, db: max |x - x*| <= 1e-2 max |x*|.
+  fp32 inputs: every quantity within 1e-5 relative (same forms, r = 1e-5).
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import sys
+from typing import Optional
+
+import numpy as np
+import torch
+
+from lm_head_projection_amd import _lib
+from lm_head_projection_amd.workloads import Workload
+
+
+def tol(dtype):
+    if dtype == torch.float32:
+        return dict(loss=1e-5, stat=1e-5, grad=1e-5)
+    return dict(loss=1e-3, stat=1e-3, grad=1e-2)
+
+
+def say(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@dataclasses.dataclass
+class GpuResult:
+    status_c: int
+    C: int
+    idx: np.ndarray
+    status_f: int
+    loss: float
+    m: np.ndarray
+    logs: np.ndarray
+    row_loss: np.ndarray
+    status_b: Optional[int] = None
+    dH: Optional[np.ndarray] = None
+    dW: Optional[np.ndarray] = None
+    db: Optional[np.ndarray] = None
+
+
+def to_np(t):
+    return None if t is None else t.detach().to("cpu", torch.float64).numpy()
+
+
+def run_gpu(wl: Workload, lam: float = 1.0, backward: bool = True, grad_ptr: bool = True,
+            dev: str = "cuda:0", keep_device: bool = False):
+    """compact -> forward -> backward through the C ABI; results on the host."""
+    H = wl.H.to(dev)
+    W = wl.W.to(dev)
+    b = None if wl.b is None else wl.b.to(dev)
+    labels = wl.labels.to(dev)
+    mask = None if wl.mask is None else wl.mask.to(torch.uint8).to(dev)
+    N, D = H.shape
+    V = W.shape[0]
+    ws = torch.empty(_lib.lce_workspace_size(N, D, V, H.dtype), dtype=torch.uint8, device=dev)
+    idx = torch.full((max(N, 1),), -7, dtype=torch.int32, device=dev)
+    st_c, C = _lib.lce_compact_valid(labels, mask, V, wl.ignore_index, idx, ws)
+    loss = torch.full((1,), float("nan"), dtype=torch.float32, device=dev)
+    m = torch.full((N,), 12345.0, dtype=torch.float32, device=dev)
+    logs = torch.full((N,), 12345.0, dtype=torch.float32, device=dev)
+    row_loss = torch.full((N,), 12345.0, dtype=torch.float32, device=dev)
+    st_f = None
+    if st_c in (_lib.LCE_OK, _lib.LCE_OK_EMPTY):
+        st_f = _lib.lce_forward(H, W, b, labels, idx, C, loss, m, logs, row_loss, ws)
+    torch.cuda.synchronize()
+    r = GpuResult(st_c, C, idx[:C].cpu().numpy().astype(np.int64), st_f,
+                  float(loss.item()), to_np(m), to_np(logs), to_np(row_loss))
+    if backward and st_f in (_lib.LCE_OK, _lib.LCE_OK_EMPTY):
+        g = torch.tensor([lam], dtype=torch.float32, device=dev) if grad_ptr else None
+        dH = torch.full_like(H, 7.0)
+        dW = torch.full_like(W, 7.0)
+        db = None if b is None else torch.full_like(b, 7.0)
+        r.status_b = _lib.lce_backward(H, W, b, labels, idx, C, m, logs, g, dH, dW, db, ws)
+        torch.cuda.synchronize()
+        if keep_device:
+            r.dH, r.dW, r.db = dH, dW, db
+        else:
+            r.dH, r.dW, r.db = to_np(dH), to_np(dW), to_np(db)
+    return r
+
+
+def max_rel_err(x, ref):
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    scale = np.max(np.abs(ref)) if ref.size else 0.0
+    err = np.max(np.abs(x - ref)) if ref.size else 0.0
+    return err / scale if scale > 0 else err
+
+
+def assert_grad_close(name, x, ref, r):
+    e = max_rel_err(x, ref)
+    assert np.all(np.isfinite(x)), f"{name}: non-finite values"
+    assert e <= r, f"{name}: max|x-ref|/max|ref| = {e:.3e} > {r:.1e}"
+    return e
+
+
+def assert_stat_close(name, x, ref, r):
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    bound = r * np.maximum(1.0, np.abs(ref))
+    bad = np.abs(x - ref) > bound
+    assert not np.any(bad), f"{name}: {int(bad.sum())} entries off, worst {np.max(np.abs(x - ref)):.3e}"
