@@ -40,7 +40,19 @@ def parse():
     p.add_argument("--workload", default="packed")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                   help="only run 3 device-to-device copies of BYTES (scales HBM byte counters) and exit")
     return p.parse_args()
+
+
+def copy_calibration(nbytes: int):
+    import torch
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": a.numel() * 4, "copies": 3}), flush=True)
 
 
 def git_rev():
@@ -97,6 +109,9 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
               "multi-GPU sharding is a design note, not part of this build.", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     import torch
     from lm_head_projection_amd import _lib
     from lm_head_projection_amd import workloads as WL

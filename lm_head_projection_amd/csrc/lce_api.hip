@@ -153,6 +153,22 @@ int choose_split(int n_rb, int n_vt) {
   return best;
 }
 
+// Vocabulary tiles per replay workgroup: minimise (waves of workgroups) x
+// (tiles per workgroup) with at most 8 tiles, ties to fewer tiles.
+int choose_tiles_per_wg(int n_rb, int vtiles) {
+  int best = 1;
+  int64_t best_cost = INT64_MAX;
+  for (int tpw = 1; tpw <= std::min(vtiles, 8); ++tpw) {
+    const int64_t waves = cdiv((int64_t)n_rb * cdiv(vtiles, tpw), kCUs);
+    const int64_t cost = waves * tpw;
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = tpw;
+    }
+  }
+  return best;
+}
+
 lce_status_t zero_bytes(void* p, int64_t bytes, hipStream_t s) {
   if (!p || bytes <= 0) return LCE_OK;
   const int64_t n16 = bytes / 16;
@@ -201,8 +217,8 @@ lce_status_t forward_impl(const T* H, const T* W, const T* b, const int64_t* lab
   const int n_split = choose_split(n_rb, n_vt);
   const int n_work = n_rb * n_split;
   const int per_xcd = (int)cdiv(n_work, 8);
-  set_lds_attr<T>((const void*)k_fwd<T>, Geo<T>::LDS_BYTES);
-  LCE_LAUNCH("k_fwd", (k_fwd<T>), per_xcd * 8, kThreads, Geo<T>::LDS_BYTES, s, W, b, Hc, yc, Cpad,
+  set_lds_attr<T>((const void*)k_fwd<T>, gemm_lds_bytes<T>());
+  LCE_LAUNCH("k_fwd", (k_fwd<T>), per_xcd * 8, kThreads, gemm_lds_bytes<T>(), s, W, b, Hc, yc, Cpad,
              (int)D, (int)V, n_rb, n_split, n_vt, n_work, per_xcd, pm, ps, tgt);
   LCE_TRY(fill_f32(m, N, -INFINITY, s));
   LCE_TRY(fill_f32(logs, N, -INFINITY, s));
@@ -247,8 +263,8 @@ lce_status_t backward_impl(const T* H, const T* W, const T* b, const int64_t* la
   const int n_rb = Cpad / Cf::BN;
   const int n_nt = (int)cdiv(D, Cf::BN);
   const int n_dh_mt = Cpad / Cf::BM;
-  set_lds_attr<T>((const void*)k_replay<T>, Geo<T>::LDS_BYTES);
-  set_lds_attr<T>((const void*)k_grad<T>, Geo<T>::LDS_BYTES);
+  set_lds_attr<T>((const void*)k_replay<T>, gemm_lds_bytes<T>());
+  set_lds_attr<T>((const void*)k_grad<T>, gemm_lds_bytes<T>());
 
   int S = 0;  // dH k-splits, fixed by the first (widest) chunk
   for (int64_t v0 = 0, chunk = 0; v0 < V; v0 += L.Vc, ++chunk) {
@@ -257,10 +273,11 @@ lce_status_t backward_impl(const T* H, const T* W, const T* b, const int64_t* la
     const int kpad = vtiles * Cf::BM;
     // K4: replay this chunk into G.
     {
-      const int n_work = n_rb * vtiles;
+      const int tpw = choose_tiles_per_wg(n_rb, vtiles);
+      const int n_work = n_rb * (int)cdiv(vtiles, tpw);
       const int per_xcd = (int)cdiv(n_work, 8);
-      LCE_LAUNCH("k_replay", (k_replay<T>), per_xcd * 8, kThreads, Geo<T>::LDS_BYTES, s, W, b, Hc,
-                 yc, mc, lsc, Cpad, (int)D, (int)V, (int)v0, n_rb, n_work, per_xcd, Gc, ldg,
+      LCE_LAUNCH("k_replay", (k_replay<T>), per_xcd * 8, kThreads, gemm_lds_bytes<T>(), s, W, b, Hc,
+                 yc, mc, lsc, Cpad, (int)D, (int)V, (int)v0, vtiles, tpw, n_rb, n_work, per_xcd, Gc, ldg,
                  db ? dbp : (float*)nullptr, lddb);
     }
     // K5: dH split so that one dH tile's K matches one dW tile's K (= Cpad).
@@ -272,9 +289,11 @@ lce_status_t backward_impl(const T* H, const T* W, const T* b, const int64_t* la
     const int S_eff = (int)cdiv(kpad, ks_len);
     const int n_dh = n_dh_mt * n_nt * S_eff;
     const int n_dw = vtiles * n_nt;
-    LCE_LAUNCH("k_grad", (k_grad<T>), n_dh + n_dw, kThreads, Geo<T>::LDS_BYTES, s, Gc, ldg, kpad, Hc,
-               W, Cpad, (int)D, (int)v0, vc, (int)(V - v0), n_nt, n_dh_mt, (int)ks_len, n_dh, vtiles, slots,
-               slot_stride, chunk == 0 ? 0 : 1, dW, grad_loss, (int)C);
+    const int n_work = n_dh + n_dw;
+    const int per_xcd = (int)cdiv(n_work, 8);
+    LCE_LAUNCH("k_grad", (k_grad<T>), per_xcd * 8, kThreads, gemm_lds_bytes<T>(), s, Gc, ldg, kpad, Hc,
+               W, Cpad, (int)D, (int)v0, vc, (int)(V - v0), n_nt, n_dh_mt, (int)ks_len, n_dh, vtiles,
+               n_work, per_xcd, slots, slot_stride, chunk == 0 ? 0 : 1, dW, grad_loss, (int)C);
   }
   {
     const int64_t vec = N * (D / 4);

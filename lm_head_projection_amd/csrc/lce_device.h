@@ -40,11 +40,11 @@ template <> __device__ __forceinline__ uint16_t from_f32<uint16_t>(float x) {
 // ---------------------------------------------------------------- tile config
 template <typename T> struct Cfg;
 template <> struct Cfg<uint16_t> {
-  static constexpr int BM = 256, BN = 256, BK = 64;
+  static constexpr int BM = 256, BN = 256, BK = 32;
   static constexpr int VEC = 8;     // elements per 16-byte vector
   static constexpr int KG = 4;      // k rows per transposed block (K-outer loader)
   static constexpr int ESZ = 2;
-  static constexpr int STRIDE = BK + 8;  // LDS row stride in elements (144 B)
+  static constexpr int STRIDE = BK + 8;  // LDS row stride in elements (80 B)
 };
 template <> struct Cfg<float> {
   static constexpr int BM = 128, BN = 128, BK = 32;
@@ -79,11 +79,13 @@ __device__ __forceinline__ int acc_row(int tm, int i, int lane) {
 // an operand need no per-vector branches.  Resources are rebased at the tile
 // (or stage) origin so every offset stays far below 2^32 bytes.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  const int64_t n = bytes < 0 ? 0 : (bytes > 0xFFFFFFFFll ? 0xFFFFFFFFll : bytes);
+  const int64_t n = bytes < 0 ? 0 : (bytes > 0xFFFFFF00ll ? 0xFFFFFF00ll : bytes);
   // Third dword: 32-bit data format, as required for raw (untyped) loads on gfx9.
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)(uint32_t)n,
                                            0x00020000);
 }
+// An offset no resource range reaches (num_records <= 0xFFFFFF00 < off).
+constexpr uint32_t kOobOffset = 0xFFFFFFF0u;
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
@@ -112,14 +114,11 @@ template <typename T, int ROWS> struct Loader<T, ROWS, true> {
     for (int j = 0; j < NV; ++j) {
       const int q = threadIdx.x + j * kThreads;
       const int rr = q / VPR, kv = q % VPR;
-      r[j] = buf_load16(rs, (uint32_t)(((int64_t)rr * ld + k0 + kv * C::VEC) * (int64_t)sizeof(T)));
-    }
-    if (k0 + C::BK > kend) {
-#pragma unroll
-      for (int j = 0; j < NV; ++j) {
-        const int kv = (threadIdx.x + j * kThreads) % VPR;
-        if (k0 + kv * C::VEC >= kend) r[j] = u32x4{0u, 0u, 0u, 0u};
-      }
+      uint32_t off = (uint32_t)(((int64_t)rr * ld + k0 + kv * C::VEC) * (int64_t)sizeof(T));
+      // A k-vector past kend gets an offset past num_records: the hardware
+      // returns 0 and no wait on the loaded value is needed.
+      if (k0 + kv * C::VEC >= kend) off = kOobOffset;
+      r[j] = buf_load16(rs, off);
     }
   }
   __device__ __forceinline__ void store(T* lds) const {
@@ -207,24 +206,34 @@ __device__ __forceinline__ void mma_stage(const T* __restrict__ As, const T* __r
   const T* a_base = As + (wm * G::WTM + lr) * C::STRIDE + lk;
   const T* b_base = Bs + (wn * G::WTN + lr) * C::STRIDE + lk;
   if constexpr (sizeof(T) == 2) {
+    // Operand fragments are double-buffered across the k-substeps: the LDS
+    // reads of substep kk+1 are in flight while substep kk's MFMAs run.
+    constexpr int KK = C::BK / 16;
+    u32x4 a[2][G::TM], b[2][G::TN];
 #pragma unroll
-    for (int kk = 0; kk < C::BK / 16; ++kk) {
-      u32x4 a[G::TM], b[G::TN];
+    for (int tm = 0; tm < G::TM; ++tm)
+      a[0][tm] = *reinterpret_cast<const u32x4*>(a_base + tm * 32 * C::STRIDE);
 #pragma unroll
-      for (int tm = 0; tm < G::TM; ++tm)
-        a[tm] = *reinterpret_cast<const u32x4*>(a_base + tm * 32 * C::STRIDE + kk * 16);
+    for (int tn = 0; tn < G::TN; ++tn)
+      b[0][tn] = *reinterpret_cast<const u32x4*>(b_base + tn * 32 * C::STRIDE);
 #pragma unroll
-      for (int tn = 0; tn < G::TN; ++tn)
-        b[tn] = *reinterpret_cast<const u32x4*>(b_base + tn * 32 * C::STRIDE + kk * 16);
+    for (int kk = 0; kk < KK; ++kk) {
+      const int cb = kk & 1, nb = cb ^ 1;
+      if (kk + 1 < KK) {
+#pragma unroll
+        for (int tm = 0; tm < G::TM; ++tm)
+          a[nb][tm] = *reinterpret_cast<const u32x4*>(a_base + tm * 32 * C::STRIDE + (kk + 1) * 16);
+#pragma unroll
+        for (int tn = 0; tn < G::TN; ++tn)
+          b[nb][tn] = *reinterpret_cast<const u32x4*>(b_base + tn * 32 * C::STRIDE + (kk + 1) * 16);
+      }
 #pragma unroll
       for (int tm = 0; tm < G::TM; ++tm)
 #pragma unroll
         for (int tn = 0; tn < G::TN; ++tn)
           acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8_t, a[tm]), __builtin_bit_cast(bf16x8_t, b[tn]),
+              __builtin_bit_cast(bf16x8_t, a[cb][tm]), __builtin_bit_cast(bf16x8_t, b[cb][tn]),
               acc[tm][tn], 0, 0, 0);
-      // Keep operand lifetimes to one k-substep (register pressure).
-      __builtin_amdgcn_sched_barrier(0);
     }
   } else {
     // fp32: lane l supplies k = kk*16 + 8*(l/32) + j to the j-th 32x32x2 MFMA;
@@ -348,5 +357,20 @@ __device__ __forceinline__ void halfwave_reduce_scatter(float (&v)[NV], int lane
 // workgroup b runs on XCD b%8.  Giving each XCD a contiguous range of work
 // items keeps the items that share operand tiles on one L2.
 __device__ __forceinline__ int xcd_remap(int b, int per_xcd) { return (b & 7) * per_xcd + (b >> 3); }
+
+// Grouped order over an (n_a x n_b) grid of work items: consecutive items
+// walk GA values of `a` before advancing `b`, so the ~32 workgroups that run
+// together on one XCD touch GA row blocks and 32/GA column blocks (their
+// operand tiles then stay in that XCD's L2).  The last group may be short.
+template <int GA>
+__device__ __forceinline__ void grouped_index(int w, int n_a, int n_b, int& a, int& b) {
+  const int per_group = GA * n_b;
+  const int g = w / per_group;
+  const int first = g * GA;
+  const int rows = min(n_a - first, GA);
+  const int r = w - g * per_group;
+  a = first + r % rows;
+  b = r / rows;
+}
 
 }  // namespace lce

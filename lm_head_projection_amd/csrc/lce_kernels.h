@@ -14,6 +14,7 @@
 #pragma once
 
 #include "lce_device.h"
+#include "lce_pipe.h"
 
 namespace lce {
 
@@ -21,6 +22,8 @@ namespace lce {
 // a_i = 1[mask_i] 1[y_i != ignore] (section 01).  Three passes: per-block
 // counts, one-block exclusive scan of the counts, ordered scatter.  No atomics.
 constexpr int kCmpBlock = 256;
+// Row blocks per L2 group in the score-tile kernels (see grouped_index).
+constexpr int kGroupRows = 8;
 
 __device__ __forceinline__ bool is_supervised(const int64_t* labels, const uint8_t* mask, int64_t i,
                                               int64_t ignore) {
@@ -191,6 +194,67 @@ __device__ __forceinline__ void add_bias(f32x16_t (&acc)[Geo<T>::TM][Geo<T>::TN]
     }
 }
 
+// Per-tile forward epilogue: bias, ragged-column mask, running (m, s) update
+// and target capture for the TN rows a lane holds.
+template <typename T>
+__device__ __forceinline__ void fwd_epilogue(f32x16_t (&acc)[Geo<T>::TM][Geo<T>::TN],
+                                             const T* __restrict__ bias, int m0, int V, const int (&row)[Geo<T>::TN],
+                                             const int (&y)[Geo<T>::TN], float (&mrun)[Geo<T>::TN],
+                                             float (&srun)[Geo<T>::TN], float* __restrict__ tgt,
+                                             int wm, int lane) {
+  using C = Cfg<T>;
+  using G = Geo<T>;
+  const int vbase = m0 + wm * G::WTM;
+  if (bias) add_bias<T>(acc, bias, vbase, V, lane);
+  if (m0 + C::BM > V) {  // ragged last tile: columns past V do not exist
+#pragma unroll
+    for (int tm = 0; tm < G::TM; ++tm)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (vbase + acc_row(tm, i, lane) >= V)
+#pragma unroll
+          for (int tn = 0; tn < G::TN; ++tn) acc[tm][tn][i] = -INFINITY;
+  }
+#pragma unroll
+  for (int tn = 0; tn < G::TN; ++tn) {
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int tm = 0; tm < G::TM; ++tm)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, acc[tm][tn][i]);
+    const float mnew = fmaxf(mrun[tn], mloc);
+    const float mref = (mnew == -INFINITY) ? 0.f : mnew;
+    float ssum = 0.f;
+    if constexpr (sizeof(T) == 4) {
+      // fp32: Z - m is exact for nearby values, so a large common shift
+      // costs no precision (section 02: compute relative to m).
+#pragma unroll
+      for (int tm = 0; tm < G::TM; ++tm)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ssum += __builtin_amdgcn_exp2f((acc[tm][tn][i] - mref) * kLog2e);
+    } else {
+      const float mneg = -mref * kLog2e;
+#pragma unroll
+      for (int tm = 0; tm < G::TM; ++tm)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ssum += __builtin_amdgcn_exp2f(fmaf(acc[tm][tn][i], kLog2e, mneg));
+    }
+    // First tile: the rescale factor of the (empty) old sum is 0.
+    const float alpha = (mnew == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f((mrun[tn] - mnew) * kLog2e);
+    srun[tn] = srun[tn] * alpha + ssum;
+    mrun[tn] = mnew;
+    // Target capture by global column id.
+    const int d = y[tn] - vbase;
+    if ((unsigned)d < (unsigned)G::WTM) {
+#pragma unroll
+      for (int tm = 0; tm < G::TM; ++tm)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (acc_row(tm, i, lane) == d) tgt[row[tn]] = acc[tm][tn][i];
+    }
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k_fwd(const T* __restrict__ W, const T* __restrict__ bias,
                                                   const T* __restrict__ Hc,
@@ -201,10 +265,10 @@ __global__ __launch_bounds__(kThreads) void k_fwd(const T* __restrict__ W, const
   using C = Cfg<T>;
   using G = Geo<T>;
   extern __shared__ __align__(16) char smem_raw[];
-  T* smem = reinterpret_cast<T*>(smem_raw);
   const int w = xcd_remap(blockIdx.x, per_xcd);
   if (w >= n_work) return;
-  const int rb = w % n_rb, split = w / n_rb;
+  int rb, split;
+  grouped_index<kGroupRows>(w, n_rb, n_split, rb, split);
   const int t0 = (int)((int64_t)split * n_vt / n_split);
   const int t1 = (int)((int64_t)(split + 1) * n_vt / n_split);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -221,63 +285,30 @@ __global__ __launch_bounds__(kThreads) void k_fwd(const T* __restrict__ W, const
     srun[tn] = 0.f;
   }
   const int nsteps = (D + C::BK - 1) / C::BK;
-
-  for (int t = t0; t < t1; ++t) {
-    const int m0 = t * C::BM;
-    const int vbase = m0 + wm * G::WTM;
+  float* red;
+  if constexpr (sizeof(T) == 2) {
     f32x16_t acc[G::TM][G::TN];
-    zero_acc<T>(acc);
-    gemm_tile<T, true, true>(W, (int64_t)V * D, D, m0, Hc, (int64_t)Cpad * D, D, n0, 0, D, nsteps,
-                           acc, smem);
-    if (bias) add_bias<T>(acc, bias, vbase, V, lane);
-
-    if (m0 + C::BM > V) {  // ragged last tile: columns past V do not exist
-#pragma unroll
-      for (int tm = 0; tm < G::TM; ++tm)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (vbase + acc_row(tm, i, lane) >= V)
-#pragma unroll
-            for (int tn = 0; tn < G::TN; ++tn) acc[tm][tn][i] = -INFINITY;
+    pipe::run<0, true>(
+        t1 - t0, nsteps, D, smem_raw, acc,
+        [&](int t, pipe::Opnd& A, pipe::Opnd& B, int& k0) {
+          A = pipe::Opnd{W, (int64_t)V * D, D, (t0 + t) * C::BM};
+          B = pipe::Opnd{Hc, (int64_t)Cpad * D, D, n0};
+          k0 = 0;
+        },
+        [&](int t, f32x16_t (&acc)[G::TM][G::TN]) {
+          fwd_epilogue<T>(acc, bias, (t0 + t) * C::BM, V, row, y, mrun, srun, tgt, wm, lane);
+        });
+    red = reinterpret_cast<float*>(smem_raw + pipe::RING_BYTES);
+  } else {
+    T* smem = reinterpret_cast<T*>(smem_raw);
+    for (int t = t0; t < t1; ++t) {
+      f32x16_t acc[G::TM][G::TN];
+      zero_acc<T>(acc);
+      gemm_tile<T, true, true>(W, (int64_t)V * D, D, t * C::BM, Hc, (int64_t)Cpad * D, D, n0, 0, D,
+                               nsteps, acc, smem);
+      fwd_epilogue<T>(acc, bias, t * C::BM, V, row, y, mrun, srun, tgt, wm, lane);
     }
-#pragma unroll
-    for (int tn = 0; tn < G::TN; ++tn) {
-      float mloc = -INFINITY;
-#pragma unroll
-      for (int tm = 0; tm < G::TM; ++tm)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, acc[tm][tn][i]);
-      const float mnew = fmaxf(mrun[tn], mloc);
-      const float mref = (mnew == -INFINITY) ? 0.f : mnew;
-      float ssum = 0.f;
-      if constexpr (sizeof(T) == 4) {
-        // fp32: Z - m is exact for nearby values, so a large common shift
-        // costs no precision (section 02: compute relative to m).
-#pragma unroll
-        for (int tm = 0; tm < G::TM; ++tm)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) ssum += __builtin_amdgcn_exp2f((acc[tm][tn][i] - mref) * kLog2e);
-      } else {
-        const float mneg = -mref * kLog2e;
-#pragma unroll
-        for (int tm = 0; tm < G::TM; ++tm)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) ssum += __builtin_amdgcn_exp2f(fmaf(acc[tm][tn][i], kLog2e, mneg));
-      }
-      // First tile: the rescale factor of the (empty) old sum is 0.
-      const float alpha = (mnew == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f((mrun[tn] - mnew) * kLog2e);
-      srun[tn] = srun[tn] * alpha + ssum;
-      mrun[tn] = mnew;
-      // Target capture by global column id.
-      const int d = y[tn] - vbase;
-      if ((unsigned)d < (unsigned)G::WTM) {
-#pragma unroll
-        for (int tm = 0; tm < G::TM; ++tm)
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (acc_row(tm, i, lane) == d) tgt[row[tn]] = acc[tm][tn][i];
-      }
-    }
+    red = reinterpret_cast<float*>(smem_raw);  // free: gemm_tile ends on a barrier
   }
 
   // Lanes l and l^32 hold the same rows (different vocabulary entries).
@@ -288,7 +319,6 @@ __global__ __launch_bounds__(kThreads) void k_fwd(const T* __restrict__ W, const
     lse_merge(mrun[tn], srun[tn], mo, so);
   }
   // Waves with the same wn and different wm hold the same rows.
-  float* red = reinterpret_cast<float*>(smem_raw);  // LDS is free: gemm_tile ends on a barrier
   static_assert(G::WGM == 2, "merge below assumes two waves per row range");
   if (wm == 1 && lane < 32) {
 #pragma unroll
@@ -308,6 +338,11 @@ __global__ __launch_bounds__(kThreads) void k_fwd(const T* __restrict__ W, const
       ps[(int64_t)split * Cpad + row[tn]] = srun[tn];
     }
   }
+}
+
+// Dynamic LDS bytes of the GEMM kernels for element type T.
+template <typename T> constexpr int gemm_lds_bytes() {
+  return sizeof(T) == 2 ? pipe::LDS_BYTES : Geo<T>::LDS_BYTES;
 }
 
 // ============================================================== K3 merge + loss
@@ -368,37 +403,25 @@ __global__ void k_inv_scatter(const int32_t* __restrict__ idx, int C, int* __res
 __global__ void k_store_scalar(float* __restrict__ p, float v) { p[0] = v; }
 
 // ============================================================== K4 replay
-// One (row block, vocabulary tile) per workgroup: recompute the score tile,
-// p = exp((Z - m) - log s) from the saved statistics, subtract 1 at the target
-// column (global id), write G = p - onehot (unscaled; lambda/C is applied in
-// the gradient epilogues) into the chunk buffer G[c][v - v0], and, with a
-// bias, the per-row-block column sums of G (db partials) in a fixed order.
+// Work item = (row block, run of `tpw` vocabulary tiles of this chunk).  For
+// each tile: recompute the score tile, p = exp((Z - m) - log s) from the
+// saved statistics, subtract 1 at the target column (global id), write
+// G = p - onehot (unscaled; lambda/C is applied in the gradient epilogues)
+// into the chunk buffer G[c][v - v0], and, with a bias, the per-row-block
+// column sums of G (db partials) in a fixed order.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void k_replay(
-    const T* __restrict__ W, const T* __restrict__ bias, const T* __restrict__ Hc,
-    const int* __restrict__ yc, const float* __restrict__ mc, const float* __restrict__ lsc, int Cpad,
-    int D, int V, int v0, int n_rb, int n_work, int per_xcd, T* __restrict__ Gc, int64_t ldg,
-    float* __restrict__ dbp, int64_t lddb) {
+__device__ __forceinline__ void replay_epilogue(f32x16_t (&acc)[Geo<T>::TM][Geo<T>::TN],
+                                                const T* __restrict__ bias, int m0, int n0, int V, int v0,
+                                                const int* __restrict__ yc, const float* __restrict__ mc,
+                                                const float* __restrict__ lsc, T* __restrict__ Gc,
+                                                int64_t ldg, float* __restrict__ dbp, int64_t lddb,
+                                                int rb, float* red, bool raw_sync) {
   using C = Cfg<T>;
   using G = Geo<T>;
-  extern __shared__ __align__(16) char smem_raw[];
-  T* smem = reinterpret_cast<T*>(smem_raw);
-  const int w = xcd_remap(blockIdx.x, per_xcd);
-  if (w >= n_work) return;
-  const int rb = w % n_rb, vt = w / n_rb;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave % G::WGM, wn = wave / G::WGM;
-  const int n0 = rb * C::BN;
-  const int m0 = v0 + vt * C::BM;
   const int vbase = m0 + wm * G::WTM;
-
-  f32x16_t acc[G::TM][G::TN];
-  zero_acc<T>(acc);
-  const int nsteps = (D + C::BK - 1) / C::BK;
-  gemm_tile<T, true, true>(W, (int64_t)V * D, D, m0, Hc, (int64_t)Cpad * D, D, n0, 0, D, nsteps,
-                           acc, smem);
   if (bias) add_bias<T>(acc, bias, vbase, V, lane);
-
 #pragma unroll
   for (int tn = 0; tn < G::TN; ++tn) {
     const int r = n0 + wn * G::WTN + tn * 32 + (lane & 31);
@@ -468,31 +491,80 @@ __global__ __launch_bounds__(kThreads) void k_replay(
   for (int tm = 0; tm < G::TM; ++tm)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      float s = 0.f;
+      float sum = 0.f;
 #pragma unroll
-      for (int tn = 0; tn < G::TN; ++tn) s += acc[tm][tn][i];
-      cs[tm * 16 + i] = s;
+      for (int tn = 0; tn < G::TN; ++tn) sum += acc[tm][tn][i];
+      cs[tm * 16 + i] = sum;
     }
   halfwave_reduce_scatter<NV>(cs, lane);
   constexpr int PER = NV / 32;
-  float* red = reinterpret_cast<float*>(smem_raw);  // free after gemm_tile's final barrier
   // red[wn][wm][lane][PER]
 #pragma unroll
   for (int j = 0; j < PER; ++j) red[((wn * G::WGM + wm) * 64 + lane) * PER + j] = cs[j];
-  __syncthreads();
+  if (raw_sync) {
+    pipe::wait_lgkm0();
+    pipe::raw_barrier();
+  } else {
+    __syncthreads();
+  }
   if (wn == 0) {
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
-      float s = red[((0 * G::WGM + wm) * 64 + lane) * PER + j];
+      float sum = red[((0 * G::WGM + wm) * 64 + lane) * PER + j];
 #pragma unroll
-      for (int q = 1; q < G::WGN; ++q) s += red[((q * G::WGM + wm) * 64 + lane) * PER + j];
+      for (int q = 1; q < G::WGN; ++q) sum += red[((q * G::WGM + wm) * 64 + lane) * PER + j];
       const int e = (lane & 31) * PER + j;
       const int v = vbase + acc_row(e >> 4, e & 15, lane);
-      if (v < V) dbp[(int64_t)rb * lddb + v] = s;
+      if (v < V) dbp[(int64_t)rb * lddb + v] = sum;
     }
   }
 }
 
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_replay(
+    const T* __restrict__ W, const T* __restrict__ bias, const T* __restrict__ Hc,
+    const int* __restrict__ yc, const float* __restrict__ mc, const float* __restrict__ lsc, int Cpad,
+    int D, int V, int v0, int vtiles, int tpw, int n_rb, int n_work, int per_xcd, T* __restrict__ Gc,
+    int64_t ldg, float* __restrict__ dbp, int64_t lddb) {
+  using C = Cfg<T>;
+  using G = Geo<T>;
+  extern __shared__ __align__(16) char smem_raw[];
+  const int w = xcd_remap(blockIdx.x, per_xcd);
+  if (w >= n_work) return;
+  int rb, vg;
+  grouped_index<kGroupRows>(w, n_rb, n_work / n_rb, rb, vg);
+  const int vt0 = vg * tpw;
+  const int ntiles = min(tpw, vtiles - vt0);
+  const int n0 = rb * C::BN;
+  const int nsteps = (D + C::BK - 1) / C::BK;
+  if constexpr (sizeof(T) == 2) {
+    float* red = reinterpret_cast<float*>(smem_raw + pipe::RING_BYTES);
+    f32x16_t acc[G::TM][G::TN];
+    pipe::run<0, true>(
+        ntiles, nsteps, D, smem_raw, acc,
+        [&](int t, pipe::Opnd& A, pipe::Opnd& B, int& k0) {
+          A = pipe::Opnd{W, (int64_t)V * D, D, v0 + (vt0 + t) * C::BM};
+          B = pipe::Opnd{Hc, (int64_t)Cpad * D, D, n0};
+          k0 = 0;
+        },
+        [&](int t, f32x16_t (&acc)[G::TM][G::TN]) {
+          replay_epilogue<T>(acc, bias, v0 + (vt0 + t) * C::BM, n0, V, v0, yc, mc, lsc, Gc, ldg, dbp, lddb,
+                             rb, red, true);
+        });
+  } else {
+    T* smem = reinterpret_cast<T*>(smem_raw);
+    for (int t = 0; t < ntiles; ++t) {
+      const int m0 = v0 + (vt0 + t) * C::BM;
+      f32x16_t acc[G::TM][G::TN];
+      zero_acc<T>(acc);
+      gemm_tile<T, true, true>(W, (int64_t)V * D, D, m0, Hc, (int64_t)Cpad * D, D, n0, 0, D, nsteps, acc,
+                               smem);
+      replay_epilogue<T>(acc, bias, m0, n0, V, v0, yc, mc, lsc, Gc, ldg, dbp, lddb, rb,
+                         reinterpret_cast<float*>(smem_raw), false);
+      __syncthreads();  // the next tile's loads reuse the LDS the db sums used
+    }
+  }
+}
 
 // ============================================================== K5 gradients
 // One launch per vocabulary chunk, two kinds of output tiles:
@@ -506,65 +578,98 @@ __global__ __launch_bounds__(kThreads) void k_replay(
 // Operands: G is K-contiguous for dH (k = v) and K-outer for dW (k = c); W
 // (k = v) and Hc (k = c) are K-outer; the loaders transpose them in registers.
 template <typename T>
+__device__ __forceinline__ void grad_store(const f32x16_t (&acc)[Geo<T>::TM][Geo<T>::TN], bool dh, int m0,
+                                           int n0, int D, int vc, int v0, float* slot, int accumulate,
+                                           T* __restrict__ dW, float scale) {
+  using G = Geo<T>;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave % G::WGM, wn = wave / G::WGM;
+#pragma unroll
+  for (int tn = 0; tn < G::TN; ++tn) {
+    const int n = n0 + wn * G::WTN + tn * 32 + (lane & 31);
+    if (n >= D) continue;
+#pragma unroll
+    for (int tm = 0; tm < G::TM; ++tm) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = m0 + wm * G::WTM + acc_row(tm, i, lane);
+        if (dh) {
+          float* p = slot + (int64_t)r * D + n;
+          *p = accumulate ? (*p + acc[tm][tn][i]) : acc[tm][tn][i];
+        } else if (r < vc) {
+          dW[(int64_t)(v0 + r) * D + n] = from_f32<T>(scale * acc[tm][tn][i]);
+        }
+      }
+      // One 32x32 block at a time keeps the read-modify-write registers bounded.
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+template <typename T>
 __global__ __launch_bounds__(kThreads) void k_grad(
     const T* __restrict__ Gc, int64_t ldg, int kpad_g, const T* __restrict__ Hc,
     const T* __restrict__ W, int Cpad, int D, int v0, int vc, int w_rows, int n_nt, int n_dh_mt, int ks_len,
-    int n_dh, int n_dw_mt, float* __restrict__ slots, int64_t slot_stride, int accumulate,
-    T* __restrict__ dW, const float* __restrict__ grad_loss, int Ctrue) {
+    int n_dh, int n_dw_mt, int n_work, int per_xcd, float* __restrict__ slots, int64_t slot_stride,
+    int accumulate, T* __restrict__ dW, const float* __restrict__ grad_loss, int Ctrue) {
   using C = Cfg<T>;
   using G = Geo<T>;
   extern __shared__ __align__(16) char smem_raw[];
-  T* smem = reinterpret_cast<T*>(smem_raw);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave % G::WGM, wn = wave / G::WGM;
-  f32x16_t acc[G::TM][G::TN];
-  zero_acc<T>(acc);
-  const int b = blockIdx.x;
-  if (b < n_dh) {
-    const int mt = b % n_dh_mt;
-    const int q = b / n_dh_mt;
-    const int nt = q % n_nt, ks = q / n_nt;
-    const int m0 = mt * C::BM, n0 = nt * C::BN;
-    const int kb = ks * ks_len;
-    const int ke_a = min(kb + ks_len, kpad_g);
-    const int nsteps = (ke_a - kb + C::BK - 1) / C::BK;
-    if (nsteps > 0)
-      gemm_tile<T, true, false>(Gc, (int64_t)Cpad * ldg, ldg, m0, W + (int64_t)v0 * D,
-                                (int64_t)w_rows * D, D, n0, kb, ke_a, nsteps, acc, smem);
-    float* slot = slots + (int64_t)ks * slot_stride;
-#pragma unroll
-    for (int tn = 0; tn < G::TN; ++tn) {
-      const int n = n0 + wn * G::WTN + tn * 32 + (lane & 31);
-      if (n >= D) continue;
-#pragma unroll
-      for (int tm = 0; tm < G::TM; ++tm)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r = m0 + wm * G::WTM + acc_row(tm, i, lane);
-          float* p = slot + (int64_t)r * D + n;
-          *p = accumulate ? (*p + acc[tm][tn][i]) : acc[tm][tn][i];
-        }
-    }
+  const int b = xcd_remap(blockIdx.x, per_xcd);
+  if (b >= n_work) return;
+  // The n_nt column tiles that share an A block are consecutive items, so
+  // they run together on one XCD and read that block through its L2.
+  const bool dh = b < n_dh;
+  int m0, n0, kb, nsteps;
+  float* slot = nullptr;
+  if (dh) {
+    const int nt = b % n_nt;
+    const int q = b / n_nt;
+    const int mt = q % n_dh_mt, ks = q / n_dh_mt;
+    m0 = mt * C::BM;
+    n0 = nt * C::BN;
+    kb = ks * ks_len;
+    const int ke = min(kb + ks_len, kpad_g);
+    nsteps = (ke - kb + C::BK - 1) / C::BK;
+    slot = slots + (int64_t)ks * slot_stride;
   } else {
     const int q = b - n_dh;
-    const int mt = q % n_dw_mt, nt = q / n_dw_mt;
-    const int m0 = mt * C::BM, n0 = nt * C::BN;
-    const int nsteps = Cpad / C::BK;
-    gemm_tile<T, false, false>(Gc, (int64_t)Cpad * ldg, ldg, m0, Hc, (int64_t)Cpad * D, D, n0, 0, Cpad,
-                               nsteps, acc, smem);
-    const float scale = (grad_loss ? grad_loss[0] : 1.f) / (float)Ctrue;
-#pragma unroll
-    for (int tn = 0; tn < G::TN; ++tn) {
-      const int n = n0 + wn * G::WTN + tn * 32 + (lane & 31);
-      if (n >= D) continue;
-#pragma unroll
-      for (int tm = 0; tm < G::TM; ++tm)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r = m0 + wm * G::WTM + acc_row(tm, i, lane);
-          if (r < vc) dW[(int64_t)(v0 + r) * D + n] = from_f32<T>(scale * acc[tm][tn][i]);
-        }
+    const int nt = q % n_nt, mt = q / n_nt;
+    m0 = mt * C::BM;
+    n0 = nt * C::BN;
+    kb = 0;
+    nsteps = Cpad / C::BK;
+  }
+  const float scale = (grad_loss ? grad_loss[0] : 1.f) / (float)Ctrue;
+  if constexpr (sizeof(T) == 2) {
+    // dH_T += G_T,B W_B: A = G (k = v contiguous), B = W rows (k-outer).
+    // dW_B = G^T Hc: A = G (k = c outer), B = Hc (k-outer).
+    f32x16_t acc[G::TM][G::TN];
+    auto origin = [&](int, pipe::Opnd& A, pipe::Opnd& B, int& k0) {
+      A = pipe::Opnd{Gc, (int64_t)Cpad * ldg, ldg, m0};
+      B = dh ? pipe::Opnd{W + (int64_t)v0 * D, (int64_t)w_rows * D, D, n0}
+             : pipe::Opnd{Hc, (int64_t)Cpad * D, D, n0};
+      k0 = kb;
+    };
+    auto no_epi = [](int, f32x16_t (&)[G::TM][G::TN]) {};
+    if (dh)
+      pipe::run<0, false>(1, nsteps, nsteps * C::BK, smem_raw, acc, origin, no_epi);
+    else
+      pipe::run<1, false>(1, nsteps, nsteps * C::BK, smem_raw, acc, origin, no_epi);
+    grad_store<T>(acc, dh, m0, n0, D, vc, v0, slot, accumulate, dW, scale);
+  } else {
+    T* smem = reinterpret_cast<T*>(smem_raw);
+    f32x16_t acc[G::TM][G::TN];
+    zero_acc<T>(acc);
+    if (dh) {
+      if (nsteps > 0)
+        gemm_tile<T, true, false>(Gc, (int64_t)Cpad * ldg, ldg, m0, W + (int64_t)v0 * D, (int64_t)w_rows * D,
+                                  D, n0, kb, kb + nsteps * C::BK, nsteps, acc, smem);
+    } else {
+      gemm_tile<T, false, false>(Gc, (int64_t)Cpad * ldg, ldg, m0, Hc, (int64_t)Cpad * D, D, n0, 0, Cpad,
+                                 nsteps, acc, smem);
     }
+    grad_store<T>(acc, dh, m0, n0, D, vc, v0, slot, accumulate, dW, scale);
   }
 }
 

@@ -1,0 +1,260 @@
+// bf16 MFMA GEMM pipeline for gfx950 built on direct-to-LDS buffer loads.
+//
+// One workgroup (8 wave64) computes a sequence of 256 x 256 output tiles.
+// Operand tiles travel global -> LDS with `buffer_load_dwordx4 ... lds`
+// (no staging registers), through a ring of NS = 4 LDS stages of BK = 32:
+// three stages are in flight while one is consumed, and the loads of the
+// next tile's first stages overlap the current tile's epilogue.  Each wave
+// waits only for its own loads (vmcnt) and one workgroup barrier per stage
+// publishes the stage and frees the slot that the next load overwrites.
+//
+// LDS layouts (per operand and stage, 16 KB):
+//  * K-contiguous operand (element (r, k) at base[r*ld + k]): [r][k], 64-byte
+//    rows of four 16-byte chunks; chunk c of row r sits in slot
+//    c ^ ((r >> 2) & 3), so the 16 rows that one ds_read_b128 phase touches
+//    fall in 16 distinct bank groups.
+//  * K-outer operand (element (r, k) at base[k*ld + r]): [k][r], exactly as in
+//    global memory, 512-byte rows; 32-byte pairs permuted by XOR with
+//    2*(k & 3).  MFMA fragments come from ds_read_b64_tr_b16: within each
+//    16-lane group, lane i receives element i%4 of lane (4j + i/4)'s 8-byte
+//    chunk for j = 0..3, i.e. four consecutive k of one r.
+#pragma once
+
+#include "lce_device.h"
+
+namespace lce {
+namespace pipe {
+
+constexpr int BM = 256, BN = 256, BK = 32, NS = 4;
+constexpr int OPND_BYTES = 256 * BK * 2;          // one operand, one stage: 16 KB
+constexpr int STAGE_BYTES = 2 * OPND_BYTES;       // A then B
+constexpr int RING_BYTES = NS * STAGE_BYTES;      // 128 KB
+constexpr int SCRATCH_BYTES = 8192;               // epilogue scratch after the ring
+constexpr int LDS_BYTES = RING_BYTES + SCRATCH_BYTES;
+constexpr int WGM = 2, WGN = 4, WTM = 128, WTN = 64, TM = 4, TN = 2;
+constexpr int DMA_PER_OPND = OPND_BYTES / 1024 / 8;  // 1 KB DMA instructions per wave: 2
+constexpr int DMA_PER_STAGE = 2 * DMA_PER_OPND;      // 4 per wave per stage
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// One operand of one output tile.
+struct Opnd {
+  const uint16_t* base;  // operand origin
+  int64_t elems;         // elements from base to the end of the operand
+  int64_t ld;            // leading dimension (elements)
+  int r0;                // first row (M or N index) of the tile
+};
+
+// s_waitcnt with only vmcnt constrained (expcnt and lgkmcnt left free).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void wait_vmcnt_rt(int n) {
+  if (n >= 2 * DMA_PER_STAGE) wait_vmcnt<2 * DMA_PER_STAGE>();
+  else if (n >= DMA_PER_STAGE) wait_vmcnt<DMA_PER_STAGE>();
+  else wait_vmcnt<0>();
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xF | (7 << 4) | (0 << 8) | (3 << 14)); }
+// Workgroup barrier without a memory fence (a fence would drain every
+// in-flight LDS load); callers wait for what they need explicitly.
+__device__ __forceinline__ void raw_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// ------------------------------------------------------------------ loads
+// Per-tile load plan of one operand: a buffer resource at the tile origin
+// and each lane's byte offsets for its DMA_PER_OPND instructions; a stage
+// only adds its k offset.  Rows past the operand's end fall past
+// num_records and load 0 in hardware.
+struct Plan {
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t voff[DMA_PER_OPND];  // byte offsets at k = k0 of the tile
+  int kc8[DMA_PER_OPND];        // K-contiguous only: k offset of the lane's chunk
+  uint32_t kstride;             // bytes per unit of k
+};
+
+template <bool KC>
+__device__ __forceinline__ void plan_opnd(Plan& p, const Opnd& o, int k0, int wave, int lane) {
+  if constexpr (KC) {
+    const int64_t base = (int64_t)o.r0 * o.ld + k0;
+    p.rs = make_rsrc(o.base + base, (o.elems - base) * 2);
+    p.kstride = 2;
+  } else {
+    const int64_t base = (int64_t)k0 * o.ld + o.r0;
+    p.rs = make_rsrc(o.base + base, (o.elems - base) * 2);
+    p.kstride = (uint32_t)(o.ld * 2);
+  }
+#pragma unroll
+  for (int i = 0; i < DMA_PER_OPND; ++i) {
+    const int q = (wave * DMA_PER_OPND + i) * 64 + lane;  // 16-byte chunk in the 16 KB tile
+    if constexpr (KC) {
+      const int row = q >> 2, slot = q & 3;
+      const int kc = slot ^ ((row >> 2) & 3);
+      p.voff[i] = (uint32_t)(((int64_t)row * o.ld + kc * 8) * 2);
+      p.kc8[i] = kc * 8;
+    } else {
+      const int kr = q >> 5, c = q & 31;
+      const int gp = (c >> 1) ^ (2 * (kr & 3));
+      p.voff[i] = (uint32_t)(((int64_t)kr * o.ld + 8 * (2 * gp + (c & 1))) * 2);
+      p.kc8[i] = 0;
+    }
+  }
+}
+
+// Issues this wave's share (DMA_PER_OPND x 1 KB) of one stage; krel = k of
+// the stage relative to the tile's k0.  K-contiguous chunks at or past krel_end
+// load 0 (only checked when the stage straddles it).
+template <bool KC>
+__device__ __forceinline__ void issue_plan(const Plan& p, int krel, int krel_end, char* lds_opnd, int wave) {
+  const uint32_t add = (uint32_t)krel * p.kstride;
+  const bool tail = KC && (krel + BK > krel_end);
+#pragma unroll
+  for (int i = 0; i < DMA_PER_OPND; ++i) {
+    uint32_t off = p.voff[i] + add;
+    if (tail && krel + p.kc8[i] >= krel_end) off = kOobOffset;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(p.rs, (lds_void*)(lds_opnd + (wave * DMA_PER_OPND + i) * 1024), 16,
+                                             off, 0, 0, 0);
+  }
+}
+
+// ------------------------------------------------------------------ fragments
+// 8 bf16 along k for MFMA lane `lane`: row/col r_base + (lane & 31),
+// k = 16*kk + 8*(lane >> 5) + 0..7.
+template <bool KC>
+__device__ __forceinline__ u32x4 load_frag(const char* lds_opnd, int r_base, int kk, int lane) {
+  if constexpr (KC) {
+    const int R = r_base + (lane & 31);
+    const int kc = 2 * kk + (lane >> 5);
+    return *reinterpret_cast<const u32x4*>(lds_opnd + R * 64 + ((kc ^ ((R >> 2) & 3)) << 4));
+  } else {
+    const int a = lane & 15;
+    const int n = r_base + 16 * ((lane >> 4) & 1) + 4 * (a & 3);
+    const int k = 16 * kk + 8 * (lane >> 5) + (a >> 2);
+    const char* p = lds_opnd + k * 512 + ((((n >> 4) ^ (2 * (k & 3)))) << 5) + ((n & 15) << 1);
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p);
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p + 4 * 512));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+    return u32x4{l2[0], l2[1], h2[0], h2[1]};
+  }
+}
+
+// A operand layout: 0 = K-contiguous, 1 = K-outer, 2 = chosen at run time by
+// a wave-uniform flag (one pipeline serves both layouts).
+template <int A_MODE>
+__device__ __forceinline__ u32x4 load_frag_a(const char* sa, int r_base, int kk, int lane, bool a_kc) {
+  if constexpr (A_MODE == 0) return load_frag<true>(sa, r_base, kk, lane);
+  else if constexpr (A_MODE == 1) return load_frag<false>(sa, r_base, kk, lane);
+  else return a_kc ? load_frag<true>(sa, r_base, kk, lane) : load_frag<false>(sa, r_base, kk, lane);
+}
+// Operand fragments of one k-substep (16 k) of one stage.
+template <int A_MODE, bool B_KC>
+struct Frags {
+  u32x4 a[TM], b[TN];
+  __device__ __forceinline__ void load(const char* st, int kk, int wm, int wn, int lane, bool a_kc) {
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) b[tn] = load_frag<B_KC>(st + OPND_BYTES, wn * WTN + tn * 32, kk, lane);
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) a[tm] = load_frag_a<A_MODE>(st, wm * WTM + tm * 32, kk, lane, a_kc);
+  }
+  __device__ __forceinline__ void mma(f32x16_t (&acc)[TM][TN]) const {
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn)
+        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[tm]),
+                                                              __builtin_bit_cast(bf16x8_t, b[tn]),
+                                                              acc[tm][tn], 0, 0, 0);
+  }
+  static constexpr int kReads = (TM * (A_MODE == 0 ? 1 : 2)) + TN * (B_KC ? 1 : 2);
+};
+
+__device__ __forceinline__ void zero(f32x16_t (&acc)[TM][TN]) {
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[tm][tn][i] = 0.f;
+}
+
+// Runs ntiles output tiles back to back through one continuous pipeline.
+//   origin(t, A, B, k0): operands of tile t and its first k;
+//   nsteps: BK-stages per tile (all tiles alike); kend: K-contiguous k bound
+//   (relative to the same origin as k0 + s*BK);
+//   epi(t, acc): consumes tile t's accumulator (registers; may use the LDS
+//   scratch after the ring, with raw_barrier + wait_lgkm0 for its own sync).
+// On return no load is in flight and every wave has passed a final barrier.
+// `acc` belongs to the caller: it is zeroed at the start of every tile and,
+// after the call, holds the last tile's sums (single-tile callers store it
+// themselves after run() instead of inside the pipelined loop).
+template <int A_MODE, bool B_KC, typename Origin, typename Epi>
+__device__ __forceinline__ void run(int ntiles, int nsteps, int kend, char* lds, f32x16_t (&acc)[TM][TN],
+                                    Origin origin, Epi epi, bool a_kc = true) {
+  static_assert(BK == 32, "Frags covers the two 16-wide k-substeps of a stage");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave % WGM, wn = wave / WGM;
+  const int total = ntiles * nsteps;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform: keeps LDS targets scalar
+  // Issue state (the next global step to load).
+  int it = 0, is = 0;
+  Plan pA, pB;
+  auto plan_tile = [&](int t) {
+    Opnd A, B;
+    int k0;
+    origin(t, A, B, k0);
+    if constexpr (A_MODE == 0) plan_opnd<true>(pA, A, k0, wave_s, lane);
+    else if constexpr (A_MODE == 1) plan_opnd<false>(pA, A, k0, wave_s, lane);
+    else if (a_kc) plan_opnd<true>(pA, A, k0, wave_s, lane);
+    else plan_opnd<false>(pA, A, k0, wave_s, lane);
+    plan_opnd<B_KC>(pB, B, k0, wave_s, lane);
+  };
+  plan_tile(0);
+  auto issue_next = [&](int g) {
+    char* st = lds + (g % NS) * STAGE_BYTES;
+    if constexpr (A_MODE == 0) issue_plan<true>(pA, is * BK, kend, st, wave_s);
+    else if constexpr (A_MODE == 1) issue_plan<false>(pA, is * BK, kend, st, wave_s);
+    else if (a_kc) issue_plan<true>(pA, is * BK, kend, st, wave_s);
+    else issue_plan<false>(pA, is * BK, kend, st, wave_s);
+    issue_plan<B_KC>(pB, is * BK, kend, st + OPND_BYTES, wave_s);
+    if (++is == nsteps) {
+      is = 0;
+      if (++it < ntiles) plan_tile(it);
+    }
+  };
+#pragma unroll
+  for (int g = 0; g < NS - 1; ++g)
+    if (g < total) issue_next(g);
+
+  // One barrier per stage: it publishes stage g (each wave waited for its
+  // own loads) and frees the slot of stage g-1 for the load of stage g+3.
+  // Per stage: all LDS fragment reads, then the next loads, then the MFMAs.
+  int t = 0, s = 0;
+  for (int g = 0; g < total; ++g) {
+    wait_vmcnt_rt(DMA_PER_STAGE * min(NS - 2, total - 1 - g));
+    raw_barrier();
+    if (s == 0) zero(acc);
+    const char* st = lds + (g % NS) * STAGE_BYTES;
+    Frags<A_MODE, B_KC> f0, f1;
+    f0.load(st, 0, wm, wn, lane, a_kc);
+    f1.load(st, 1, wm, wn, lane, a_kc);
+    if (g + NS - 1 < total) issue_next(g + NS - 1);
+    f0.mma(acc);
+    f1.mma(acc);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * Frags<A_MODE, B_KC>::kReads, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * TM * TN, 0);
+    if (++s == nsteps) {
+      epi(t, acc);
+      s = 0;
+      ++t;
+    }
+  }
+  raw_barrier();
+}
+
+}  // namespace pipe
+}  // namespace lce
