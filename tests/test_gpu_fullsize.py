@@ -1,0 +1,90 @@
+"""HIP path at the full workload sizes, in the launch configuration the
+benchmark times (same N, D, V; the C-ABI picks tiles, splits and chunks from
+the sizes alone).
+
+Two kinds of checks, because the float64 oracle cannot afford all C rows:
+  * full supervision: m, log s, per-row CE and dH at sampled rows, each row
+    recomputed by the oracle over the full vocabulary; the loss equals the
+    mean of the per-row CE; sum_v db_v = 0 and sum_v dW_v = 0 (softmax rows
+    sum to one) within bf16 rounding of the outputs;
+  * sparse supervision (a mask that keeps 48 rows of the same inputs):
+    every output element against the oracle.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from lm_head_projection_amd import _lib
+from lm_head_projection_amd import workloads as WL
+
+from lce_harness import assert_grad_close, assert_stat_close, run_gpu, say, tol
+
+pytestmark = pytest.mark.gpu
+
+FULL = ("sft", "page2", "packed", "stress")
+_cache = {}
+
+
+def workload(name):
+    if name not in _cache:
+        say(f"[fullsize] building workload {name}")
+        wl = WL.make_workload(name)
+        _cache[name] = (wl, wl.W.double().numpy(), None if wl.b is None else wl.b.double().numpy())
+    return _cache[name]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_fullsize_sampled_rows_and_invariants(name):
+    wl, Wd, bd = workload(name)
+    say(f"[fullsize] {name}: GPU run N={wl.N} D={wl.D} V={wl.V}")
+    r = run_gpu(wl)
+    assert r.status_c == _lib.LCE_OK and r.status_f == _lib.LCE_OK and r.status_b == _lib.LCE_OK
+    _, idx, C = O.supervised_rows(wl.labels.numpy(), None if wl.mask is None else wl.mask.numpy())
+    assert r.C == C
+    np.testing.assert_array_equal(r.idx, idx)
+    t = tol(wl.dtype)
+    # loss is the mean of the per-row CE (fp64 sum of the fp32 row values)
+    assert abs(r.loss - np.sum(r.row_loss[idx]) / C) <= 1e-6 * abs(r.loss)
+    rng = np.random.default_rng(17)
+    rows = np.sort(rng.choice(idx, size=8, replace=False))
+    rows = np.unique(np.concatenate([rows, idx[[0, -1]]]))
+    say(f"[fullsize] {name}: oracle on {rows.size} sampled rows")
+    Hs = wl.H[rows].double().numpy()
+    ys = wl.labels.numpy()[rows]
+    m, ls, l = O.rows_forward(Hs, Wd, bd, ys)
+    assert_stat_close("m", r.m[rows], m, t["stat"])
+    assert_stat_close("logs", r.logs[rows], ls, t["stat"])
+    assert_stat_close("row_loss", r.row_loss[rows], l, t["stat"])
+    dh = O.rows_grad_h(Hs, Wd, bd, ys, 1.0 / C)
+    assert_grad_close("dH rows", r.dH[rows], dh, t["grad"])
+    a = np.zeros(wl.N, dtype=bool)
+    a[idx] = True
+    assert np.all(r.dH[~a] == 0.0)
+    # softmax rows sum to one => the vocabulary sums of db and dW vanish
+    u = 2.0 ** -8  # bf16 rounding of each output element
+    if r.db is not None:
+        assert abs(np.sum(r.db)) <= u * np.sum(np.abs(r.db)) + 1e-12
+    col = np.abs(np.sum(r.dW, axis=0))
+    assert np.all(col <= u * np.sum(np.abs(r.dW), axis=0) + 1e-12)
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_fullsize_sparse_supervision_elementwise(name):
+    wl, Wd, bd = workload(name)
+    sub = WL.supervised_subset(wl, 48)
+    say(f"[fullsize] {name}: GPU run with 48 supervised rows")
+    r = run_gpu(sub)
+    say(f"[fullsize] {name}: oracle on the 48 rows")
+    f, g = O.dense_forward_backward(sub.H.double().numpy(), Wd, bd, sub.labels.numpy(), sub.mask.numpy(), 1.0)
+    t = tol(wl.dtype)
+    assert r.C == f.C == 48
+    np.testing.assert_array_equal(r.idx, f.idx)
+    assert abs(r.loss - f.loss) <= t["loss"] * abs(f.loss)
+    assert_stat_close("m", r.m[f.idx], f.m[f.idx], t["stat"])
+    assert_stat_close("logs", r.logs[f.idx], f.logs[f.idx], t["stat"])
+    assert_grad_close("dH", r.dH, g.dH, t["grad"])
+    assert_grad_close("dW", r.dW, g.dW, t["grad"])
+    if wl.b is not None:
+        assert_grad_close("db", r.db, g.db, t["grad"])
