@@ -10,7 +10,9 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "liblce.so")
+# LCE_LIBRARY may name another build of the same library (e.g. to compare two
+# builds in one process); by default the in-tree build is used.
+LIB_PATH = os.environ.get("LCE_LIBRARY") or os.path.join(PKG, "liblce.so")
 
 LCE_DTYPE_F32 = 0
 LCE_DTYPE_BF16 = 1

@@ -16,9 +16,13 @@ using namespace lce;
 
 namespace {
 
-constexpr int64_t kVcMax = 32768;     // vocabulary chunk of the gradient tile store
+#ifndef LCE_VOCAB_CHUNK
+#define LCE_VOCAB_CHUNK 32768
+#endif
+constexpr int64_t kVcMax = LCE_VOCAB_CHUNK;  // vocabulary chunk of the gradient tile store
 constexpr int kMaxSplit = 64;         // vocabulary splits of the forward pass
-constexpr int kMaxDhSlots = 4;        // k-splits of the dH GEMM
+constexpr int kDhSlotRows = 4;        // the dH slots hold 4 x Npad rows of D fp32 values
+constexpr int kMaxDhSlots = 16;       // k-splits of the dH GEMM (at most)
 constexpr int kCUs = 256;             // MI355X compute units (one 512-thread workgroup each)
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -125,7 +129,7 @@ bool make_layout(int64_t N, int64_t D, int64_t V, lce_dtype_t dt, Layout& L) {
   L.lsc = take(L.Npad * 4);
   L.inv = take(std::max<int64_t>(N, 1) * 4);
   L.G = take(L.Npad * L.Vc * esz);
-  L.slots = take((int64_t)kMaxDhSlots * L.Npad * D * 4);
+  L.slots = take((int64_t)kDhSlotRows * L.Npad * D * 4);
   L.dbp = take((L.Npad / bn) * L.Vpad * 4);
   L.total = std::max(off, fwd_end);
   return true;
@@ -148,6 +152,53 @@ int choose_split(int n_rb, int n_vt) {
     if (cost < best_cost) {
       best_cost = cost;
       best = ns;
+    }
+  }
+  return best;
+}
+
+// Makespan of k_grad's schedule: each of the 8 XCDs takes an equal share of
+// the n_a items of length L_a and of the n_b items of length L_b, and runs its
+// share on its kCUs/8 workgroup slots, the longer kind first, each item on the
+// slot that frees first (the dispatcher's order).
+int64_t makespan(int64_t n_a, int64_t L_a, int64_t n_b, int64_t L_b) {
+  int64_t worst = 0;
+  for (int x = 0; x < 8; ++x) {
+    std::vector<int64_t> slot(kCUs / 8, 0);
+    auto place = [&](int64_t n, int64_t L) {
+      for (int64_t i = 0; i < n; ++i) {
+        auto it = std::min_element(slot.begin(), slot.end());
+        *it += L;
+      }
+    };
+    const int64_t ca = (x + 1) * n_a / 8 - x * n_a / 8, cb = (x + 1) * n_b / 8 - x * n_b / 8;
+    if (L_a >= L_b) {
+      place(ca, L_a);
+      place(cb, L_b);
+    } else {
+      place(cb, L_b);
+      place(ca, L_a);
+    }
+    worst = std::max(worst, *std::max_element(slot.begin(), slot.end()));
+  }
+  return worst;
+}
+
+// dH k-splits for one chunk: the split count whose grouped launch (dH tiles of
+// K = chunk/S next to dW tiles of K = Cpad) has the shortest makespan.
+// S is bounded by the slot memory: S x Cpad rows must fit in kDhSlotRows x Npad.
+int choose_dh_splits(int64_t kpad, int64_t Cpad, int64_t Npad, int64_t n_dh_tiles_per_split, int64_t n_dw_tiles,
+                     int bk) {
+  int best = 1;
+  int64_t best_t = INT64_MAX;
+  const int s_max = (int)std::max<int64_t>(1, std::min<int64_t>(kMaxDhSlots, kDhSlotRows * Npad / Cpad));
+  for (int S = 1; S <= s_max; ++S) {
+    const int64_t ks_len = rup(cdiv(kpad, S), bk);
+    const int64_t S_eff = cdiv(kpad, ks_len);
+    const int64_t t = makespan(n_dh_tiles_per_split * S_eff, ks_len + 2 * bk, n_dw_tiles, Cpad + 2 * bk);
+    if (t < best_t) {
+      best_t = t;
+      best = S;
     }
   }
   return best;
@@ -281,19 +332,17 @@ lce_status_t backward_impl(const T* H, const T* W, const T* b, const int64_t* la
                  db ? dbp : (float*)nullptr, lddb);
     }
     // K5: dH split so that one dH tile's K matches one dW tile's K (= Cpad).
-    if (chunk == 0) {
-      const double ratio = (double)kpad / (double)Cpad;
-      S = (int)std::max<int64_t>(1, std::min<int64_t>(kMaxDhSlots, (int64_t)(ratio + 0.5)));
-    }
+    if (chunk == 0)
+      S = choose_dh_splits(kpad, Cpad, L.Npad, (int64_t)n_dh_mt * n_nt, (int64_t)vtiles * n_nt, Cf::BK);
     int64_t ks_len = rup(cdiv(kpad, S), Cf::BK);
     const int S_eff = (int)cdiv(kpad, ks_len);
     const int n_dh = n_dh_mt * n_nt * S_eff;
     const int n_dw = vtiles * n_nt;
-    const int n_work = n_dh + n_dw;
-    const int per_xcd = (int)cdiv(n_work, 8);
+    const int per_xcd = (int)(cdiv(n_dh, 8) + cdiv(n_dw, 8));
+    const int dh_first = ks_len >= Cpad ? 1 : 0;
     LCE_LAUNCH("k_grad", (k_grad<T>), per_xcd * 8, kThreads, gemm_lds_bytes<T>(), s, Gc, ldg, kpad, Hc,
                W, Cpad, (int)D, (int)v0, vc, (int)(V - v0), n_nt, n_dh_mt, (int)ks_len, n_dh, vtiles,
-               n_work, per_xcd, slots, slot_stride, chunk == 0 ? 0 : 1, dW, grad_loss, (int)C);
+               dh_first, slots, slot_stride, chunk == 0 ? 0 : 1, dW, grad_loss, (int)C);
   }
   {
     const int64_t vec = N * (D / 4);

@@ -173,6 +173,36 @@ __global__ __launch_bounds__(256) void k_gather(const T* __restrict__ H,
 // column id.  The vocabulary is the MFMA M axis, so a lane's 64 scores of a
 // row lie in its own registers and the tile needs no cross-lane reduction;
 // lanes merge once per split.  Output: partial (m, s) per (split, row).
+// The LDS bias slice arrives in whole dwords, so where V ends inside one the
+// last values are zero: the ragged last tile rewrites its slice element by
+// element (all waves reach this for the same tile).
+__device__ __noinline__ void refill_bias_slice(const uint16_t* slice, const uint16_t* __restrict__ bias, int m0,
+                                               int V) {
+  uint16_t* s = const_cast<uint16_t*>(slice);
+  if (threadIdx.x < 256) s[threadIdx.x] = (m0 + (int)threadIdx.x < V) ? bias[m0 + threadIdx.x] : (uint16_t)0;
+  pipe::wait_lgkm0();
+  pipe::raw_barrier();
+}
+
+// Adds b_v from the tile's LDS bias slice (bf16 pipeline).
+__device__ __forceinline__ void add_bias_lds(f32x16_t (&acc)[Geo<uint16_t>::TM][Geo<uint16_t>::TN],
+                                             const uint16_t* slice, int vloc0, int lane) {
+  using G = Geo<uint16_t>;
+#pragma unroll
+  for (int tm = 0; tm < G::TM; ++tm)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int j = vloc0 + tm * 32 + 8 * i4 + 4 * (lane >> 5);
+      const u32x2 w = *reinterpret_cast<const u32x2*>(slice + j);
+      const float bv[4] = {to_f32((uint16_t)(w[0] & 0xFFFFu)), to_f32((uint16_t)(w[0] >> 16)),
+                           to_f32((uint16_t)(w[1] & 0xFFFFu)), to_f32((uint16_t)(w[1] >> 16))};
+#pragma unroll
+      for (int tn = 0; tn < G::TN; ++tn)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[tm][tn][i4 * 4 + r] += bv[r];
+    }
+}
+
 // Adds b_v to every score of the tile after the K loop (one rounding, so a
 // large bias does not coarsen the fp32 partial sums of H.W).
 template <typename T>
@@ -201,11 +231,18 @@ __device__ __forceinline__ void fwd_epilogue(f32x16_t (&acc)[Geo<T>::TM][Geo<T>:
                                              const T* __restrict__ bias, int m0, int V, const int (&row)[Geo<T>::TN],
                                              const int (&y)[Geo<T>::TN], float (&mrun)[Geo<T>::TN],
                                              float (&srun)[Geo<T>::TN], float* __restrict__ tgt,
-                                             int wm, int lane) {
+                                             int wm, int lane, const uint16_t* bias_slice = nullptr) {
   using C = Cfg<T>;
   using G = Geo<T>;
   const int vbase = m0 + wm * G::WTM;
-  if (bias) add_bias<T>(acc, bias, vbase, V, lane);
+  if constexpr (sizeof(T) == 2) {
+    if (bias) {
+      if (m0 + C::BM > V) refill_bias_slice(bias_slice, reinterpret_cast<const uint16_t*>(bias), m0, V);
+      add_bias_lds(acc, bias_slice, wm * G::WTM, lane);
+    }
+  } else {
+    if (bias) add_bias<T>(acc, bias, vbase, V, lane);
+  }
   if (m0 + C::BM > V) {  // ragged last tile: columns past V do not exist
 #pragma unroll
     for (int tm = 0; tm < G::TM; ++tm)
@@ -296,8 +333,10 @@ __global__ __launch_bounds__(kThreads) void k_fwd(const T* __restrict__ W, const
           k0 = 0;
         },
         [&](int t, f32x16_t (&acc)[G::TM][G::TN]) {
-          fwd_epilogue<T>(acc, bias, (t0 + t) * C::BM, V, row, y, mrun, srun, tgt, wm, lane);
-        });
+          fwd_epilogue<T>(acc, bias, (t0 + t) * C::BM, V, row, y, mrun, srun, tgt, wm, lane,
+                          pipe::bias_slice(smem_raw, t));
+        },
+        true, reinterpret_cast<const uint16_t*>(bias), V);
     red = reinterpret_cast<float*>(smem_raw + pipe::RING_BYTES);
   } else {
     T* smem = reinterpret_cast<T*>(smem_raw);
@@ -415,13 +454,21 @@ __device__ __forceinline__ void replay_epilogue(f32x16_t (&acc)[Geo<T>::TM][Geo<
                                                 const int* __restrict__ yc, const float* __restrict__ mc,
                                                 const float* __restrict__ lsc, T* __restrict__ Gc,
                                                 int64_t ldg, float* __restrict__ dbp, int64_t lddb,
-                                                int rb, float* red, bool raw_sync) {
+                                                int rb, float* red, bool raw_sync,
+                                                const uint16_t* bias_slice = nullptr) {
   using C = Cfg<T>;
   using G = Geo<T>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave % G::WGM, wn = wave / G::WGM;
   const int vbase = m0 + wm * G::WTM;
-  if (bias) add_bias<T>(acc, bias, vbase, V, lane);
+  if constexpr (sizeof(T) == 2) {
+    if (bias) {
+      if (m0 + C::BM > V) refill_bias_slice(bias_slice, reinterpret_cast<const uint16_t*>(bias), m0, V);
+      add_bias_lds(acc, bias_slice, wm * G::WTM, lane);
+    }
+  } else {
+    if (bias) add_bias<T>(acc, bias, vbase, V, lane);
+  }
 #pragma unroll
   for (int tn = 0; tn < G::TN; ++tn) {
     const int r = n0 + wn * G::WTN + tn * 32 + (lane & 31);
@@ -460,6 +507,7 @@ __device__ __forceinline__ void replay_epilogue(f32x16_t (&acc)[Geo<T>::TM][Geo<
           for (int tn = 0; tn < G::TN; ++tn) acc[tm][tn][i] = 0.f;
   }
   // Store G (4 consecutive vocabulary entries of one row per lane and group).
+  // bf16: blocked layout (256 x 32 blocks, see gblock_offset); fp32: row-major.
 #pragma unroll
   for (int tn = 0; tn < G::TN; ++tn) {
     const int r = n0 + wn * G::WTN + tn * 32 + (lane & 31);
@@ -474,7 +522,8 @@ __device__ __forceinline__ void replay_epilogue(f32x16_t (&acc)[Geo<T>::TM][Geo<
                               ((uint32_t)from_f32<uint16_t>(acc[tm][tn][i4 * 4 + 1]) << 16);
           const uint32_t hi = (uint32_t)from_f32<uint16_t>(acc[tm][tn][i4 * 4 + 2]) |
                               ((uint32_t)from_f32<uint16_t>(acc[tm][tn][i4 * 4 + 3]) << 16);
-          *reinterpret_cast<u32x2*>(grow + off) = u32x2{lo, hi};
+          *reinterpret_cast<u32x2*>(Gc + pipe::gblock_offset(r, (int64_t)(vbase - v0 + off), ldg / pipe::GB_COLS)) =
+              u32x2{lo, hi};
         } else {
           *reinterpret_cast<f32x4_t*>(grow + off) =
               f32x4_t{acc[tm][tn][i4 * 4 + 0], acc[tm][tn][i4 * 4 + 1], acc[tm][tn][i4 * 4 + 2],
@@ -540,7 +589,9 @@ __global__ __launch_bounds__(kThreads) void k_replay(
   if constexpr (sizeof(T) == 2) {
     float* red = reinterpret_cast<float*>(smem_raw + pipe::RING_BYTES);
     f32x16_t acc[G::TM][G::TN];
-    pipe::run<0, true>(
+    // Each wave's epilogue ends with TN*TM*4 G-tile stores (plus, with a
+    // bias, the db stores of some waves).
+    pipe::run<0, true, G::TN * G::TM * 4>(
         ntiles, nsteps, D, smem_raw, acc,
         [&](int t, pipe::Opnd& A, pipe::Opnd& B, int& k0) {
           A = pipe::Opnd{W, (int64_t)V * D, D, v0 + (vt0 + t) * C::BM};
@@ -549,8 +600,9 @@ __global__ __launch_bounds__(kThreads) void k_replay(
         },
         [&](int t, f32x16_t (&acc)[G::TM][G::TN]) {
           replay_epilogue<T>(acc, bias, v0 + (vt0 + t) * C::BM, n0, V, v0, yc, mc, lsc, Gc, ldg, dbp, lddb,
-                             rb, red, true);
-        });
+                             rb, red, true, pipe::bias_slice(smem_raw, t));
+        },
+        true, reinterpret_cast<const uint16_t*>(bias), V);
   } else {
     T* smem = reinterpret_cast<T*>(smem_raw);
     for (int t = 0; t < ntiles; ++t) {
@@ -610,15 +662,28 @@ template <typename T>
 __global__ __launch_bounds__(kThreads) void k_grad(
     const T* __restrict__ Gc, int64_t ldg, int kpad_g, const T* __restrict__ Hc,
     const T* __restrict__ W, int Cpad, int D, int v0, int vc, int w_rows, int n_nt, int n_dh_mt, int ks_len,
-    int n_dh, int n_dw_mt, int n_work, int per_xcd, float* __restrict__ slots, int64_t slot_stride,
+    int n_dh, int n_dw_mt, int dh_first, float* __restrict__ slots, int64_t slot_stride,
     int accumulate, T* __restrict__ dW, const float* __restrict__ grad_loss, int Ctrue) {
   using C = Cfg<T>;
   using G = Geo<T>;
   extern __shared__ __align__(16) char smem_raw[];
-  const int b = xcd_remap(blockIdx.x, per_xcd);
-  if (b >= n_work) return;
-  // The n_nt column tiles that share an A block are consecutive items, so
-  // they run together on one XCD and read that block through its L2.
+  // Workgroups go to the 8 XCDs round-robin.  Each XCD takes an equal share of
+  // the dH items and of the dW items (their K differ), the longer kind first,
+  // so that every XCD finishes at about the same time.  Within a share the
+  // n_nt column tiles that share an A block are consecutive, so they run
+  // together and read that block through the XCD's L2.
+  const int n_dw = n_dw_mt * n_nt;
+  int b;
+  {
+    const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
+    const int dh_lo = (int)((int64_t)x * n_dh / 8), dh_cnt = (int)((int64_t)(x + 1) * n_dh / 8) - dh_lo;
+    const int dw_lo = (int)((int64_t)x * n_dw / 8), dw_cnt = (int)((int64_t)(x + 1) * n_dw / 8) - dw_lo;
+    if (dh_first)
+      b = j < dh_cnt ? dh_lo + j : (j - dh_cnt < dw_cnt ? n_dh + dw_lo + (j - dh_cnt) : -1);
+    else
+      b = j < dw_cnt ? n_dh + dw_lo + j : (j - dw_cnt < dh_cnt ? dh_lo + (j - dw_cnt) : -1);
+  }
+  if (b < 0) return;
   const bool dh = b < n_dh;
   int m0, n0, kb, nsteps;
   float* slot = nullptr;
@@ -645,8 +710,15 @@ __global__ __launch_bounds__(kThreads) void k_grad(
     // dH_T += G_T,B W_B: A = G (k = v contiguous), B = W rows (k-outer).
     // dW_B = G^T Hc: A = G (k = c outer), B = Hc (k-outer).
     f32x16_t acc[G::TM][G::TN];
+    // G is stored blocked (gblock_offset with ldg/32 blocks per row block).
+    const int64_t nvb = ldg / pipe::GB_COLS;
     auto origin = [&](int, pipe::Opnd& A, pipe::Opnd& B, int& k0) {
-      A = pipe::Opnd{Gc, (int64_t)Cpad * ldg, ldg, m0};
+      if (dh)  // rows c of one 256-row block, k = v: 32 x 256 blocks along k
+        A = pipe::Opnd{Gc + (int64_t)(m0 / pipe::GB_ROWS) * nvb * pipe::GB_ELEMS,
+                       (int64_t)Cpad * ldg - (int64_t)(m0 / pipe::GB_ROWS) * nvb * pipe::GB_ELEMS, pipe::GB_COLS, 0,
+                       pipe::GB_ELEMS / pipe::GB_COLS, 0};
+      else     // rows v, k = c: the blocked layout read transposed
+        A = pipe::Opnd{Gc, (int64_t)Cpad * ldg, ldg, m0, 1, nvb * pipe::GB_ELEMS};
       B = dh ? pipe::Opnd{W + (int64_t)v0 * D, (int64_t)w_rows * D, D, n0}
              : pipe::Opnd{Hc, (int64_t)Cpad * D, D, n0};
       k0 = kb;

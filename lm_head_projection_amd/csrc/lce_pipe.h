@@ -29,8 +29,15 @@ constexpr int BM = 256, BN = 256, BK = 32, NS = 4;
 constexpr int OPND_BYTES = 256 * BK * 2;          // one operand, one stage: 16 KB
 constexpr int STAGE_BYTES = 2 * OPND_BYTES;       // A then B
 constexpr int RING_BYTES = NS * STAGE_BYTES;      // 128 KB
-constexpr int SCRATCH_BYTES = 8192;               // epilogue scratch after the ring
-constexpr int LDS_BYTES = RING_BYTES + SCRATCH_BYTES;
+constexpr int SCRATCH_BYTES = 4096;               // epilogue scratch after the ring
+constexpr int BIAS_SLOTS = 4, BIAS_SLOT_BYTES = 1024;  // per-tile bias slices after the scratch
+constexpr int BIAS_OFFSET = RING_BYTES + SCRATCH_BYTES;
+constexpr int LDS_BYTES = BIAS_OFFSET + BIAS_SLOTS * BIAS_SLOT_BYTES;
+
+// LDS copy of the bias slice of tile t (element j = bias[m0(t) + j], 0 past V).
+__device__ __forceinline__ const uint16_t* bias_slice(const char* lds, int t) {
+  return reinterpret_cast<const uint16_t*>(lds + BIAS_OFFSET + (t & (BIAS_SLOTS - 1)) * BIAS_SLOT_BYTES);
+}
 constexpr int WGM = 2, WGN = 4, WTM = 128, WTN = 64, TM = 4, TN = 2;
 constexpr int DMA_PER_OPND = OPND_BYTES / 1024 / 8;  // 1 KB DMA instructions per wave: 2
 constexpr int DMA_PER_STAGE = 2 * DMA_PER_OPND;      // 4 per wave per stage
@@ -39,12 +46,26 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
 // One operand of one output tile.
+//   K-contiguous: element (r, k) at base[r*ld + k*kstep] for k a multiple of
+//     32, plus k%32 (kstep = 1 for plain row-major; 256 for the blocked G
+//     layout, whose 256 x 32 blocks follow each other along k).
+//   K-outer: element (r, k) at base[k*ld + r], or, with bstride > 0 (blocked
+//     G read transposed), at base[(k/256)*bstride + (k%256)*32 + (r/32)*8192 + r%32].
 struct Opnd {
   const uint16_t* base;  // operand origin
   int64_t elems;         // elements from base to the end of the operand
   int64_t ld;            // leading dimension (elements)
   int r0;                // first row (M or N index) of the tile
+  int64_t kstep = 1;     // K-contiguous only (see above)
+  int64_t bstride = 0;   // K-outer only: > 0 selects the blocked layout
 };
+
+// Blocked G: 256 rows (c) x 32 columns (v) per 16 KB block; blocks of one row
+// block follow each other along v, row blocks are `nvb` blocks apart.
+constexpr int GB_ROWS = 256, GB_COLS = 32, GB_ELEMS = GB_ROWS * GB_COLS;
+__host__ __device__ __forceinline__ int64_t gblock_offset(int64_t c, int64_t v, int64_t nvb) {
+  return ((c / GB_ROWS) * nvb + v / GB_COLS) * GB_ELEMS + (c % GB_ROWS) * GB_COLS + v % GB_COLS;
+}
 
 // s_waitcnt with only vmcnt constrained (expcnt and lgkmcnt left free).
 template <int N>
@@ -52,8 +73,14 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
+// Waits until at most `n` vector memory operations are outstanding, for the
+// n this pipeline produces: k*DMA_PER_STAGE (k = 0..2) plus optionally `extra`
+// younger operations (stores an epilogue issued after those loads).
+template <int EXTRA>
 __device__ __forceinline__ void wait_vmcnt_rt(int n) {
-  if (n >= 2 * DMA_PER_STAGE) wait_vmcnt<2 * DMA_PER_STAGE>();
+  if (n >= 2 * DMA_PER_STAGE + EXTRA) wait_vmcnt<2 * DMA_PER_STAGE + EXTRA>();
+  else if (n >= DMA_PER_STAGE + EXTRA) wait_vmcnt<DMA_PER_STAGE + EXTRA>();
+  else if (n >= 2 * DMA_PER_STAGE) wait_vmcnt<2 * DMA_PER_STAGE>();
   else if (n >= DMA_PER_STAGE) wait_vmcnt<DMA_PER_STAGE>();
   else wait_vmcnt<0>();
 }
@@ -75,15 +102,23 @@ struct Plan {
   __amdgpu_buffer_rsrc_t rs;
   uint32_t voff[DMA_PER_OPND];  // byte offsets at k = k0 of the tile
   int kc8[DMA_PER_OPND];        // K-contiguous only: k offset of the lane's chunk
-  uint32_t kstride;             // bytes per unit of k
+  uint32_t kstride;             // bytes per unit of k (stages are 32-aligned)
+  uint32_t bstride_b;           // K-outer blocked: bytes between 256-row blocks (0 = plain)
 };
 
 template <bool KC>
 __device__ __forceinline__ void plan_opnd(Plan& p, const Opnd& o, int k0, int wave, int lane) {
+  p.bstride_b = 0;
   if constexpr (KC) {
-    const int64_t base = (int64_t)o.r0 * o.ld + k0;
+    const int64_t base = (int64_t)o.r0 * o.ld + (int64_t)k0 * o.kstep;
     p.rs = make_rsrc(o.base + base, (o.elems - base) * 2);
-    p.kstride = 2;
+    p.kstride = (uint32_t)(o.kstep * 2);
+  } else if (o.bstride > 0) {
+    // k0 is a multiple of 256 here (it is 0 for the transposed-G operand).
+    const int64_t base = (int64_t)(k0 / GB_ROWS) * o.bstride + (int64_t)(o.r0 / GB_COLS) * GB_ELEMS;
+    p.rs = make_rsrc(o.base + base, (o.elems - base) * 2);
+    p.kstride = GB_COLS * 2;
+    p.bstride_b = (uint32_t)(o.bstride * 2);
   } else {
     const int64_t base = (int64_t)k0 * o.ld + o.r0;
     p.rs = make_rsrc(o.base + base, (o.elems - base) * 2);
@@ -100,7 +135,11 @@ __device__ __forceinline__ void plan_opnd(Plan& p, const Opnd& o, int k0, int wa
     } else {
       const int kr = q >> 5, c = q & 31;
       const int gp = (c >> 1) ^ (2 * (kr & 3));
-      p.voff[i] = (uint32_t)(((int64_t)kr * o.ld + 8 * (2 * gp + (c & 1))) * 2);
+      const int gv = 8 * (2 * gp + (c & 1));  // first r of the lane's 16-byte chunk
+      if (o.bstride > 0)
+        p.voff[i] = (uint32_t)(((int64_t)kr * GB_COLS + (gv / GB_COLS) * GB_ELEMS + gv % GB_COLS) * 2);
+      else
+        p.voff[i] = (uint32_t)(((int64_t)kr * o.ld + gv) * 2);
       p.kc8[i] = 0;
     }
   }
@@ -111,7 +150,11 @@ __device__ __forceinline__ void plan_opnd(Plan& p, const Opnd& o, int k0, int wa
 // load 0 (only checked when the stage straddles it).
 template <bool KC>
 __device__ __forceinline__ void issue_plan(const Plan& p, int krel, int krel_end, char* lds_opnd, int wave) {
-  const uint32_t add = (uint32_t)krel * p.kstride;
+  // Blocked K-outer: a stage stays inside one 256-row block (stages are 32
+  // rows, blocks 256), so the stage offset is block base + row offset.
+  uint32_t add = (uint32_t)krel * p.kstride;
+  if constexpr (!KC)
+    if (p.bstride_b) add = (uint32_t)(krel / GB_ROWS) * p.bstride_b + (uint32_t)(krel % GB_ROWS) * p.kstride;
   const bool tail = KC && (krel + BK > krel_end);
 #pragma unroll
   for (int i = 0; i < DMA_PER_OPND; ++i) {
@@ -192,9 +235,19 @@ __device__ __forceinline__ void zero(f32x16_t (&acc)[TM][TN]) {
 // `acc` belongs to the caller: it is zeroed at the start of every tile and,
 // after the call, holds the last tile's sums (single-tile callers store it
 // themselves after run() instead of inside the pipelined loop).
-template <int A_MODE, bool B_KC, typename Origin, typename Epi>
+// EPI_STORES: vector memory operations every wave's epilogue certainly
+// issues after its last load wait (an undercount is safe: the wait after an
+// epilogue then also drains some of them).  Vector memory operations retire
+// in issue order on this target, so younger stores need not be waited for.
+// With `bias` (A K-contiguous, A.r0 = the tile's first vocabulary row),
+// wave 0 also loads each tile's 256 bias values into bias_slice(lds, t),
+// right before that tile's first stage: the stage wait that publishes the
+// stage publishes the slice too.  A slot is reloaded 4 tiles later, after the
+// barrier that follows the last epilogue that read it ((4-1)*nsteps >= 3).
+template <int A_MODE, bool B_KC, int EPI_STORES = 0, typename Origin, typename Epi>
 __device__ __forceinline__ void run(int ntiles, int nsteps, int kend, char* lds, f32x16_t (&acc)[TM][TN],
-                                    Origin origin, Epi epi, bool a_kc = true) {
+                                    Origin origin, Epi epi, bool a_kc = true,
+                                    const uint16_t* bias = nullptr, int V = 0) {
   static_assert(BK == 32, "Frags covers the two 16-wide k-substeps of a stage");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave % WGM, wn = wave / WGM;
@@ -203,10 +256,12 @@ __device__ __forceinline__ void run(int ntiles, int nsteps, int kend, char* lds,
   // Issue state (the next global step to load).
   int it = 0, is = 0;
   Plan pA, pB;
+  int bias_m0 = 0;
   auto plan_tile = [&](int t) {
     Opnd A, B;
     int k0;
     origin(t, A, B, k0);
+    bias_m0 = A.r0;
     if constexpr (A_MODE == 0) plan_opnd<true>(pA, A, k0, wave_s, lane);
     else if constexpr (A_MODE == 1) plan_opnd<false>(pA, A, k0, wave_s, lane);
     else if (a_kc) plan_opnd<true>(pA, A, k0, wave_s, lane);
@@ -216,6 +271,11 @@ __device__ __forceinline__ void run(int ntiles, int nsteps, int kend, char* lds,
   plan_tile(0);
   auto issue_next = [&](int g) {
     char* st = lds + (g % NS) * STAGE_BYTES;
+    if (bias != nullptr && is == 0 && wave_s == 0) {
+      const __amdgpu_buffer_rsrc_t rb = make_rsrc(bias + bias_m0, (int64_t)(V - bias_m0) * 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(lds + BIAS_OFFSET + (it & (BIAS_SLOTS - 1)) * BIAS_SLOT_BYTES),
+                                               16, (uint32_t)lane * 16, 0, 0, 0);
+    }
     if constexpr (A_MODE == 0) issue_plan<true>(pA, is * BK, kend, st, wave_s);
     else if constexpr (A_MODE == 1) issue_plan<false>(pA, is * BK, kend, st, wave_s);
     else if (a_kc) issue_plan<true>(pA, is * BK, kend, st, wave_s);
@@ -235,7 +295,13 @@ __device__ __forceinline__ void run(int ntiles, int nsteps, int kend, char* lds,
   // Per stage: all LDS fragment reads, then the next loads, then the MFMAs.
   int t = 0, s = 0;
   for (int g = 0; g < total; ++g) {
-    wait_vmcnt_rt(DMA_PER_STAGE * min(NS - 2, total - 1 - g));
+    // Stage g must have landed; later stages already issued may stay in
+    // flight, and so may the stores of an epilogue that ran just before.
+    const int later = DMA_PER_STAGE * min(NS - 2, total - 1 - g);
+    if (EPI_STORES > 0 && s == 0 && g > 0 && later > 0)
+      wait_vmcnt_rt<EPI_STORES>(later + EPI_STORES);
+    else
+      wait_vmcnt_rt<0>(later);
     raw_barrier();
     if (s == 0) zero(acc);
     const char* st = lds + (g % NS) * STAGE_BYTES;
