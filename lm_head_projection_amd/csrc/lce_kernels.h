@@ -506,30 +506,51 @@ __device__ __forceinline__ void replay_epilogue(f32x16_t (&acc)[Geo<T>::TM][Geo<
 #pragma unroll
           for (int tn = 0; tn < G::TN; ++tn) acc[tm][tn][i] = 0.f;
   }
-  // Store G (4 consecutive vocabulary entries of one row per lane and group).
-  // bf16: blocked layout (256 x 32 blocks, see gblock_offset); fp32: row-major.
+  if constexpr (sizeof(T) == 2) {
+    // Store G in the blocked layout (256 x 32 blocks, see gblock_offset).  One
+    // (tm, tn) accumulator block is 32 rows c x 32 entries v, i.e. 32 whole
+    // 64-byte block rows.  Lane l (l < 32) holds entries {8j..8j+3} of row l,
+    // lane l+32 entries {8j+4..8j+7}; one permlane32 swap per register pair
+    // leaves lane l with entries 0..15 and lane l+32 with 16..31, each
+    // written as 32 contiguous bytes.
+    const int h = lane >> 5;
+    T* gb = Gc + ((int64_t)(n0 / pipe::GB_ROWS) * (ldg / pipe::GB_COLS) + (vbase - v0) / pipe::GB_COLS) *
+                     pipe::GB_ELEMS +
+            (wn * G::WTN + (lane & 31)) * pipe::GB_COLS + 16 * h;
 #pragma unroll
-  for (int tn = 0; tn < G::TN; ++tn) {
-    const int r = n0 + wn * G::WTN + tn * 32 + (lane & 31);
-    T* grow = Gc + (int64_t)r * ldg + (vbase - v0);
+    for (int tn = 0; tn < G::TN; ++tn)
 #pragma unroll
-    for (int tm = 0; tm < G::TM; ++tm)
+      for (int tm = 0; tm < G::TM; ++tm) {
+        uint32_t d[8];
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int off = tm * 32 + 8 * i4 + 4 * (lane >> 5);
-        if constexpr (sizeof(T) == 2) {
-          const uint32_t lo = (uint32_t)from_f32<uint16_t>(acc[tm][tn][i4 * 4 + 0]) |
-                              ((uint32_t)from_f32<uint16_t>(acc[tm][tn][i4 * 4 + 1]) << 16);
-          const uint32_t hi = (uint32_t)from_f32<uint16_t>(acc[tm][tn][i4 * 4 + 2]) |
-                              ((uint32_t)from_f32<uint16_t>(acc[tm][tn][i4 * 4 + 3]) << 16);
-          *reinterpret_cast<u32x2*>(Gc + pipe::gblock_offset(r, (int64_t)(vbase - v0 + off), ldg / pipe::GB_COLS)) =
-              u32x2{lo, hi};
-        } else {
-          *reinterpret_cast<f32x4_t*>(grow + off) =
+        for (int k = 0; k < 8; ++k)
+          d[k] = (uint32_t)from_f32<uint16_t>(acc[tm][tn][2 * k]) |
+                 ((uint32_t)from_f32<uint16_t>(acc[tm][tn][2 * k + 1]) << 16);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          // lanes 32..63 of d[k] <-> lanes 0..31 of d[k + 4]
+          const auto sw = __builtin_amdgcn_permlane32_swap(d[k], d[k + 4], false, false);
+          d[k] = sw[0];
+          d[k + 4] = sw[1];
+        }
+        T* dst = gb + tm * pipe::GB_ELEMS + tn * 32 * pipe::GB_COLS;
+        *reinterpret_cast<u32x4*>(dst) = u32x4{d[0], d[1], d[4], d[5]};
+        *reinterpret_cast<u32x4*>(dst + 8) = u32x4{d[2], d[3], d[6], d[7]};
+      }
+  } else {
+    // Store G row-major (4 consecutive vocabulary entries of one row per lane and group).
+#pragma unroll
+    for (int tn = 0; tn < G::TN; ++tn) {
+      const int r = n0 + wn * G::WTN + tn * 32 + (lane & 31);
+      T* grow = Gc + (int64_t)r * ldg + (vbase - v0);
+#pragma unroll
+      for (int tm = 0; tm < G::TM; ++tm)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4)
+          *reinterpret_cast<f32x4_t*>(grow + tm * 32 + 8 * i4 + 4 * (lane >> 5)) =
               f32x4_t{acc[tm][tn][i4 * 4 + 0], acc[tm][tn][i4 * 4 + 1], acc[tm][tn][i4 * 4 + 2],
                       acc[tm][tn][i4 * 4 + 3]};
-        }
-      }
+    }
   }
   if (dbp == nullptr) return;
   // Column sums over this workgroup's rows: first the TN rows a lane holds,
@@ -589,9 +610,9 @@ __global__ __launch_bounds__(kThreads) void k_replay(
   if constexpr (sizeof(T) == 2) {
     float* red = reinterpret_cast<float*>(smem_raw + pipe::RING_BYTES);
     f32x16_t acc[G::TM][G::TN];
-    // Each wave's epilogue ends with TN*TM*4 G-tile stores (plus, with a
+    // Each wave's epilogue ends with TN*TM*2 G-tile stores (plus, with a
     // bias, the db stores of some waves).
-    pipe::run<0, true, G::TN * G::TM * 4>(
+    pipe::run<0, true, G::TN * G::TM * 2>(
         ntiles, nsteps, D, smem_raw, acc,
         [&](int t, pipe::Opnd& A, pipe::Opnd& B, int& k0) {
           A = pipe::Opnd{W, (int64_t)V * D, D, v0 + (vt0 + t) * C::BM};
