@@ -68,6 +68,28 @@ def kernel_flops(C, D, V):
     return {"k_fwd": 2.0 * C * D * V, "k_replay": 2.0 * C * D * V, "k_grad": 4.0 * C * D * V}
 
 
+def stored_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` on `workload`, from the committed
+    counter profile profiles/<kernel>_<workload>_hbm_traffic.md, or None when
+    there is none or the library sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    from lm_head_projection_amd.build import source_digest
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            line = line.strip().strip("`")
+            for key in ("source_sha256", "fetch_bytes_per_launch", "write_bytes_per_launch"):
+                if line.startswith(key + ":"):
+                    vals[key] = line.split(":", 1)[1].strip()
+    if len(vals) != 3 or vals["source_sha256"] != source_digest():
+        return None
+    return {"fetch_bytes_per_launch": float(vals["fetch_bytes_per_launch"]),
+            "write_bytes_per_launch": float(vals["write_bytes_per_launch"]),
+            "path": os.path.relpath(path, ROOT)}
+
+
 def cpu_baseline(wl, target_s: float):
     """The oracle as it stands, on a bounded sample of supervised rows."""
     import numpy as np
@@ -161,7 +183,6 @@ def main():
     assert torch.isfinite(loss).all()
 
     # Timed region: K steps bracketed by synchronisation; HIP events on the stream.
-    _lib.profile_start(65536)
     torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
@@ -172,11 +193,19 @@ def main():
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    kern = _lib.profile_stop()
     total_ms = ev0.elapsed_time(ev1)
     ms = total_ms / args.steps
     peak_extra = torch.cuda.max_memory_allocated() - base_alloc
     log(f"[bench] {args.steps} steps: {ms:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f} ms/step), C={C}")
+
+    # Per-kernel durations: the same K steps again, with the library recording
+    # a HIP event pair around each of its launches on the launch stream.
+    _lib.profile_start(65536)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    kern = _lib.profile_stop()
+    log(f"[bench] per-kernel pass done ({sum(v[0] for v in kern.values()) / args.steps:.3f} ms/step in kernels)")
 
     flops_step = 8.0 * C * D * V
     tflops = flops_step / (ms * 1e-3) / 1e12
@@ -190,10 +219,15 @@ def main():
             e["tflops"] = kf[name] * args.steps / (tot * 1e-3) / 1e12
         kernels[name] = e
     dom = max((k for k in kernels if k in kf), key=lambda k: kernels[k]["total_ms_per_step"])
+    tr = stored_traffic(dom, args.workload)
     rf = {"bound": "mfma", "achieved": kernels[dom]["tflops"], "peak": peak, "unit": "TFLOP/s",
-          "frac": kernels[dom]["tflops"] / peak, "traffic": None, "kernel": dom,
+          "frac": kernels[dom]["tflops"] / peak,
+          "traffic": None if tr is None else tr["fetch_bytes_per_launch"] + tr["write_bytes_per_launch"],
+          "kernel": dom,
           "flops_per_launch": kf[dom] / kernels[dom]["launches_per_step"],
-          "avg_launch_ms": kernels[dom]["avg_ms"]}
+          "avg_launch_ms": kernels[dom]["avg_ms"],
+          "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+          "traffic_source": None if tr is None else tr["path"]}
 
     cpu = None
     if not args.no_cpu_baseline:
