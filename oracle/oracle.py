@@ -160,13 +160,67 @@ def dense_forward(H, W, b, labels, mask=None, ignore_index: int = IGNORE_INDEX,
     return ForwardResult(loss, m, logs, row_loss, idx, C, False)
 
 
+def reduce_rows(row_loss, idx, C: int, reduction: str = "mean", loss_weights=None,
+                num_label_tokens: Optional[float] = None):
+    """The loss under one of the reductions of the NeMo AutoModel chunked_ce
+    page (ChunkedCrossEntropy.forward: `reduction`, `num_label_tokens`, which
+    divides a sum-reduced loss, and `loss_weights`, constant multipliers for
+    the sum only):
+
+        mean: (1/C) sum_{i in idx} l_i           (glenzli.com section 01 objective)
+        sum:  (sum_{i in idx} w_i l_i) / n       w = 1 without weights,
+                                                 n = num_label_tokens (1 if None)
+        none: l_i per position (0 on unsupervised positions)
+    """
+    row_loss = np.asarray(row_loss, dtype=np.float64)
+    if reduction == "none":
+        out = np.zeros_like(row_loss)
+        out[idx] = row_loss[idx]
+        return out
+    if C == 0:
+        return 0.0
+    if reduction == "mean":
+        return math.fsum(row_loss[idx].tolist()) / C
+    if reduction == "sum":
+        w = np.ones_like(row_loss) if loss_weights is None else np.asarray(loss_weights, dtype=np.float64)
+        total = math.fsum((w[idx] * row_loss[idx]).tolist())
+        return total / num_label_tokens if num_label_tokens else total
+    raise ValueError(f"unknown reduction {reduction!r}")
+
+
+def row_factors(N: int, idx, C: int, reduction: str = "mean", grad=1.0, loss_weights=None,
+                num_label_tokens: Optional[float] = None) -> np.ndarray:
+    """r_i = dJ/dl_i on supervised rows (0 elsewhere), for J = grad * L with
+    the mean or sum reduction above, or J = sum_i grad_i l_i for "none"
+    (grad then holds one upstream value per position).  With dl_i/dZ_ij =
+    p_ij - 1[j = y_i] (glenzli.com section 04; AIInfraGuide section 6.6), the
+    score gradient of row i is r_i (p_i - onehot(y_i)).
+    """
+    r = np.zeros(N)
+    if C == 0:
+        return r
+    if reduction == "none":
+        g = np.broadcast_to(np.asarray(grad, dtype=np.float64), (N,))
+        r[idx] = g[idx]
+    elif reduction == "mean":
+        r[idx] = float(grad) / C
+    elif reduction == "sum":
+        w = np.ones(N) if loss_weights is None else np.asarray(loss_weights, dtype=np.float64)
+        r[idx] = float(grad) * w[idx] / (num_label_tokens if num_label_tokens else 1.0)
+    else:
+        raise ValueError(f"unknown reduction {reduction!r}")
+    return r
+
+
 def dense_backward(H, W, b, labels, m, logs, lam: float = 1.0, mask=None,
                    ignore_index: int = IGNORE_INDEX,
-                   row_block: Optional[int] = None) -> BackwardResult:
+                   row_block: Optional[int] = None,
+                   row_factor: Optional[np.ndarray] = None) -> BackwardResult:
     """dH, dW, db of lam * L (section 04 and AIInfraGuide section 6.6).
 
     p is rebuilt from the saved statistics as exp((Z - m) - log s); the target
-    column gets -1; rows are scaled by lam / C.
+    column gets -1; rows are scaled by lam / C, or by row_factor[i] (a
+    per-position array from row_factors) when it is given.
     """
     H = _f64(H)
     W = _f64(W)
@@ -187,7 +241,7 @@ def dense_backward(H, W, b, labels, m, logs, lam: float = 1.0, mask=None,
         Z = logits(H[rows], W, b)
         P = np.exp((Z - m[rows][:, None]) - logs[rows][:, None])
         P[np.arange(rows.size), y[rows]] -= 1.0
-        G = scale * P
+        G = scale * P if row_factor is None else np.asarray(row_factor, dtype=np.float64)[rows][:, None] * P
         dH[rows] = G @ W
         dW += G.T @ H[rows]
         db += G.sum(axis=0)

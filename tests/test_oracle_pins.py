@@ -394,3 +394,113 @@ def test_row_block_is_only_a_memory_bound():
     f2, g2 = O.dense_forward_backward(H, W, b, y, mask, 1.0, row_block=37)
     assert f1.loss == pytest.approx(f2.loss, rel=1e-14)
     np.testing.assert_allclose(g1.dW, g2.dW, rtol=1e-11, atol=1e-18)
+
+
+# ---------------------------------------------------------------- reductions (NeMo interface)
+def _torch_rows(H, W, b, y, mask):
+    """Per-position CE from torch's own reduction='none' (library routine)."""
+    y_eff = torch.tensor(np.where(mask, y, -100))
+    Ht = torch.tensor(H, requires_grad=True)
+    Wt = torch.tensor(W, requires_grad=True)
+    bt = torch.tensor(b, requires_grad=True)
+    ce = torch.nn.functional.cross_entropy(Ht @ Wt.T + bt, y_eff, ignore_index=-100, reduction="none")
+    return Ht, Wt, bt, y_eff, ce
+
+
+def test_sum_reduction_matches_torch_sum():
+    """reduction='sum' without weights or divisor is torch's own 'sum'
+    reduction (NeMo chunked_ce page, ChunkedCrossEntropy: reduction 'sum')."""
+    H, W, b, y, mask = _case(N=23, D=5, V=29, seed=31)
+    Ht, Wt, bt, y_eff, _ = _torch_rows(H, W, b, y, mask)
+    loss = torch.nn.functional.cross_entropy(Ht @ Wt.T + bt, y_eff, ignore_index=-100, reduction="sum")
+    loss.backward()
+    f = O.dense_forward(H, W, b, y, mask)
+    assert O.reduce_rows(f.row_loss, f.idx, f.C, "sum") == pytest.approx(loss.item(), rel=1e-12)
+    r = O.row_factors(H.shape[0], f.idx, f.C, "sum", 1.0)
+    g = O.dense_backward(H, W, b, y, f.m, f.logs, mask=mask, row_factor=r)
+    np.testing.assert_allclose(g.dH, Ht.grad.numpy(), rtol=1e-10, atol=1e-15)
+    np.testing.assert_allclose(g.dW, Wt.grad.numpy(), rtol=1e-10, atol=1e-15)
+    np.testing.assert_allclose(g.db, bt.grad.numpy(), rtol=1e-10, atol=1e-15)
+
+
+def test_weighted_sum_with_divisor_matches_torch_autograd():
+    """Weighted sum divided by num_label_tokens, with an upstream gradient:
+    torch's per-position CE (reduction='none') weighted and summed, then
+    differentiated by autograd (NeMo chunked_ce page: loss_weights are
+    constant multipliers, num_label_tokens normalises the sum)."""
+    H, W, b, y, mask = _case(N=19, D=4, V=17, seed=32)
+    rng = np.random.default_rng(33)
+    w = rng.uniform(-0.5, 2.0, H.shape[0])
+    n, lam = 57.0, 1.7
+    Ht, Wt, bt, y_eff, ce = _torch_rows(H, W, b, y, mask)
+    loss = (torch.tensor(w) * ce).sum() / n
+    (lam * loss).backward()
+    f = O.dense_forward(H, W, b, y, mask)
+    assert O.reduce_rows(f.row_loss, f.idx, f.C, "sum", w, n) == pytest.approx(loss.item(), rel=1e-12)
+    r = O.row_factors(H.shape[0], f.idx, f.C, "sum", lam, w, n)
+    g = O.dense_backward(H, W, b, y, f.m, f.logs, mask=mask, row_factor=r)
+    np.testing.assert_allclose(g.dH, Ht.grad.numpy(), rtol=1e-10, atol=1e-15)
+    np.testing.assert_allclose(g.dW, Wt.grad.numpy(), rtol=1e-10, atol=1e-15)
+    np.testing.assert_allclose(g.db, bt.grad.numpy(), rtol=1e-10, atol=1e-15)
+
+
+def test_none_reduction_matches_torch_per_position():
+    """reduction='none': per-position losses equal torch's reduction='none'
+    (0 at ignored positions); with an upstream gradient per position the
+    gradients equal autograd's (NeMo chunked_ce page: losses shaped [...])."""
+    H, W, b, y, mask = _case(N=21, D=6, V=11, seed=34)
+    g_up = np.random.default_rng(35).standard_normal(H.shape[0])
+    Ht, Wt, bt, y_eff, ce = _torch_rows(H, W, b, y, mask)
+    (torch.tensor(g_up) * ce).sum().backward()
+    f = O.dense_forward(H, W, b, y, mask)
+    np.testing.assert_allclose(O.reduce_rows(f.row_loss, f.idx, f.C, "none"), ce.detach().numpy(),
+                               rtol=1e-12, atol=0)
+    r = O.row_factors(H.shape[0], f.idx, f.C, "none", g_up)
+    assert np.all(r[~np.isin(np.arange(H.shape[0]), f.idx)] == 0.0)
+    g = O.dense_backward(H, W, b, y, f.m, f.logs, mask=mask, row_factor=r)
+    np.testing.assert_allclose(g.dH, Ht.grad.numpy(), rtol=1e-10, atol=1e-15)
+    np.testing.assert_allclose(g.dW, Wt.grad.numpy(), rtol=1e-10, atol=1e-15)
+    np.testing.assert_allclose(g.db, bt.grad.numpy(), rtol=1e-10, atol=1e-15)
+
+
+def test_weighted_sum_finite_differences():
+    """Central differences of the weighted, divided sum on every entry of H,
+    W and b (AIInfraGuide 6.9)."""
+    N, D, V = 6, 3, 5
+    rng = np.random.default_rng(36)
+    H = rng.standard_normal((N, D))
+    W = 0.8 * rng.standard_normal((V, D))
+    b = 0.5 * rng.standard_normal(V)
+    y = rng.integers(0, V, N)
+    y[2] = -100
+    w = rng.uniform(0.1, 3.0, N)
+    n, lam, eps = 4.0, 0.9, 1e-6
+
+    def J(H_, W_, b_):
+        f_ = O.dense_forward(H_, W_, b_, y)
+        return lam * O.reduce_rows(f_.row_loss, f_.idx, f_.C, "sum", w, n)
+
+    f = O.dense_forward(H, W, b, y)
+    g = O.dense_backward(H, W, b, y, f.m, f.logs, row_factor=O.row_factors(N, f.idx, f.C, "sum", lam, w, n))
+    for arr, grad in ((H, g.dH), (W, g.dW), (b, g.db)):
+        it = np.nditer(arr, flags=["multi_index"])
+        for _ in it:
+            k = it.multi_index
+            old = arr[k]
+            arr[k] = old + eps
+            jp = J(H, W, b)
+            arr[k] = old - eps
+            jm = J(H, W, b)
+            arr[k] = old
+            fd = (jp - jm) / (2 * eps)
+            assert abs(fd - grad[k]) <= 1e-7 * max(1.0, abs(grad[k])), (k, fd, grad[k])
+
+
+def test_reductions_empty_supervision():
+    """C = 0: the sum is 0 and per-position losses are all 0 (section 01 C=0
+    rule carried to the other reductions); every row factor is 0."""
+    y = np.full(4, -100)
+    f = O.dense_forward(np.ones((4, 2)), np.ones((3, 2)), None, y)
+    assert O.reduce_rows(f.row_loss, f.idx, f.C, "sum", np.ones(4), 9.0) == 0.0
+    assert np.all(O.reduce_rows(f.row_loss, f.idx, f.C, "none") == 0.0)
+    assert np.all(O.row_factors(4, f.idx, f.C, "none", np.ones(4)) == 0.0)
