@@ -23,6 +23,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "fused linear-CE fwd+bwd tokens/s and TFLOP/s (% of bf16 MFMA peak)"
+METRIC_FWD = "fused linear-CE forward-only loss tokens/s and TFLOP/s (% of bf16 MFMA peak)"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA (published)
 PEAK_FP32_TFLOPS = 157.3      # MI355X fp32 matrix (published)
 PEAK_HBM_GBS = 8000.0
@@ -38,6 +39,10 @@ def parse():
     p.add_argument("--steps", type=int, default=12)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="packed")
+    p.add_argument("--mode", choices=("train", "forward"), default="train",
+                   help="train: compaction + forward + backward; forward: compaction + forward-only loss")
+    p.add_argument("--reduction", choices=("mean", "sum", "none"), default="mean",
+                   help="mean: plain entries; sum (per-position weights, divisor N) / none: the _ex entries")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -64,7 +69,9 @@ def git_rev():
 
 
 # Algorithmic FLOPs per step, by kernel (2*C*D*V per GEMM pass).
-def kernel_flops(C, D, V):
+def kernel_flops(C, D, V, mode="train"):
+    if mode == "forward":
+        return {"k_fwd": 2.0 * C * D * V}
     return {"k_fwd": 2.0 * C * D * V, "k_replay": 2.0 * C * D * V, "k_grad": 4.0 * C * D * V}
 
 
@@ -90,7 +97,7 @@ def stored_traffic(kernel: str, workload: str):
             "path": os.path.relpath(path, ROOT)}
 
 
-def cpu_baseline(wl, target_s: float):
+def cpu_baseline(wl, target_s: float, forward_only: bool = False):
     """The oracle as it stands, on a bounded sample of supervised rows."""
     import numpy as np
     try:
@@ -109,7 +116,10 @@ def cpu_baseline(wl, target_s: float):
     def run(rows):
         sel = idx[:rows]
         t0 = time.perf_counter()
-        O.dense_forward_backward(H[sel], W, b, y[sel], None, 1.0, wl.ignore_index)
+        if forward_only:
+            O.dense_forward(H[sel], W, b, y[sel], None, wl.ignore_index)
+        else:
+            O.dense_forward_backward(H[sel], W, b, y[sel], None, 1.0, wl.ignore_index)
         return time.perf_counter() - t0
 
     n = 16
@@ -122,7 +132,7 @@ def cpu_baseline(wl, target_s: float):
         n, t = n2, run(n2)
     return {"value": n / t, "unit": "supervised tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{n} of {C} supervised rows of the {wl.name} workload (full D={wl.D}, V={wl.V}); "
-                      f"float64 NumPy dense forward+backward, {t:.1f} s"}
+                      f"float64 NumPy dense {'forward' if forward_only else 'forward+backward'}, {t:.1f} s"}
 
 
 def main():
@@ -166,13 +176,35 @@ def main():
     logs = torch.empty(N, dtype=torch.float32, device=dev)
     grad = torch.ones(1, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
+    red = _lib.REDUCTIONS[args.reduction]
+    weights, num = None, 0.0
+    if args.reduction == "sum":
+        gen = torch.Generator().manual_seed(77)
+        weights = torch.rand(N, generator=gen).to(dev)
+        num = float(N)
+    if args.reduction == "none":
+        loss = torch.empty(N, dtype=torch.float32, device=dev)
+        gen = torch.Generator().manual_seed(78)
+        grad = torch.randn(N, generator=gen).to(dev)
+    plain = args.reduction == "mean"
+    train = args.mode == "train"
 
     def step():
         st, C = _lib.lce_compact_valid(labels, mask, V, wl.ignore_index, idx, ws, stream)
         assert st == _lib.LCE_OK, _lib.status_string(st)
-        st = _lib.lce_forward(H, W, b, labels, idx, C, loss, m, logs, None, ws, stream)
+        if plain and train:
+            st = _lib.lce_forward(H, W, b, labels, idx, C, loss, m, logs, None, ws, stream)
+        else:  # the _ex entry; forward-only runs without saved statistics
+            st = _lib.lce_forward_ex(H, W, b, labels, idx, C, red, weights, num, loss,
+                                     m if train else None, logs if train else None, ws, stream)
         assert st == _lib.LCE_OK, _lib.status_string(st)
-        st = _lib.lce_backward(H, W, b, labels, idx, C, m, logs, grad, dH, dW, db, ws, stream)
+        if not train:
+            return C
+        if plain:
+            st = _lib.lce_backward(H, W, b, labels, idx, C, m, logs, grad, dH, dW, db, ws, stream)
+        else:
+            st = _lib.lce_backward_ex(H, W, b, labels, idx, C, red, weights, num, m, logs, grad, dH, dW, db,
+                                      ws, stream)
         assert st == _lib.LCE_OK, _lib.status_string(st)
         return C
 
@@ -181,6 +213,8 @@ def main():
         log(f"[bench] warmup {i + 1}/{args.warmup} done")
     torch.cuda.synchronize()
     assert torch.isfinite(loss).all()
+    if not train:
+        log("[bench] forward-only: compaction + forward, no saved statistics")
 
     # Timed region: K steps bracketed by synchronisation; HIP events on the stream.
     torch.cuda.synchronize()
@@ -207,10 +241,10 @@ def main():
     kern = _lib.profile_stop()
     log(f"[bench] per-kernel pass done ({sum(v[0] for v in kern.values()) / args.steps:.3f} ms/step in kernels)")
 
-    flops_step = 8.0 * C * D * V
+    flops_step = (8.0 if train else 2.0) * C * D * V
     tflops = flops_step / (ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if wl.dtype == torch.bfloat16 else PEAK_FP32_TFLOPS
-    kf = kernel_flops(C, D, V)
+    kf = kernel_flops(C, D, V, args.mode)
     kernels = {}
     for name, (tot, n) in sorted(kern.items(), key=lambda kv: -kv[1][0]):
         e = {"total_ms_per_step": tot / args.steps, "launches_per_step": n / args.steps,
@@ -232,11 +266,11 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on a bounded sample (host cores)")
-        cpu = cpu_baseline(wl, args.cpu_seconds)
+        cpu = cpu_baseline(wl, args.cpu_seconds, forward_only=not train)
         log(f"[bench] oracle: {cpu['value']:.1f} tok/s on {cpu['cores']} threads")
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC if train else METRIC_FWD,
         "value": C * args.steps / (total_ms * 1e-3),
         "unit": "supervised tokens/s",
         "n_gpus": 1,
@@ -249,7 +283,8 @@ def main():
         "dtype": "bf16" if wl.dtype == torch.bfloat16 else "f32",
         "data": "synthetic",
         "config": {"workload": args.workload, "N": N, "D": D, "V": V, "C": C,
-                   "bias": b is not None, "mask": mask is not None},
+                   "bias": b is not None, "mask": mask is not None, "mode": args.mode,
+                   "reduction": args.reduction},
         "tflops": tflops,
         "pct_peak": 100.0 * tflops / peak,
         "positions_per_s": N * args.steps / (total_ms * 1e-3),

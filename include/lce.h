@@ -60,6 +60,20 @@ typedef enum {
   LCE_ERR_UNSUPPORTED = -5 /* shape outside the documented limits */
 } lce_status_t;
 
+/* Reduction of the per-row cross-entropy l_i = log sum_j exp(Z_ij) - Z_{i,y_i}
+ * over the supervised rows (NeMo AutoModel chunked_ce page,
+ * ChunkedCrossEntropy.forward: `reduction`, `num_label_tokens`,
+ * `loss_weights`):
+ *   MEAN  L = (1/C) sum_i l_i                      (the page-2 objective)
+ *   SUM   L = (sum_i w_i l_i) / n                  w_i = loss_weights[i] (1 if
+ *         NULL), n = num_label_tokens (1 if 0)
+ *   NONE  the per-position values l_i (0 on unsupervised positions). */
+typedef enum {
+  LCE_REDUCTION_MEAN = 0,
+  LCE_REDUCTION_SUM = 1,
+  LCE_REDUCTION_NONE = 2
+} lce_reduction_t;
+
 /* Bytes of device workspace that lce_compact_valid, lce_forward and
  * lce_backward need for these sizes (worst case C = N).  It never grows with
  * N x V: the largest pieces are the gathered supervised rows (N x D), one
@@ -115,6 +129,40 @@ lce_status_t lce_backward(const void* H, const void* W, const void* b, const int
                           lce_dtype_t dt, const float* m, const float* logs,
                           const float* grad_loss, void* dH, void* dW, void* db, void* ws,
                           size_t ws_bytes, void* stream);
+
+/* Forward pass with a chosen reduction; also the forward-only (evaluation)
+ * entry: m and logs may be NULL when no backward call follows.
+ *   reduction         see lce_reduction_t.
+ *   loss_weights      float[N] device or NULL; per-position weights, SUM only
+ *                     (LCE_ERR_ARG with another reduction).
+ *   num_label_tokens  SUM only: divisor n > 0, or 0 for none (LCE_ERR_ARG if
+ *                     negative, infinite, NaN, or nonzero with MEAN / NONE).
+ *   loss              MEAN / SUM: float[1]; NONE: float[N] (per-position l_i,
+ *                     0 on unsupervised positions).  Device, written.
+ *   m, logs           float[N] device or NULL; as in lce_forward.
+ * Other arguments and the C == 0 behaviour (loss 0, LCE_OK_EMPTY) as in
+ * lce_forward.  The per-row values are those of lce_forward; the sums are
+ * float64 in a fixed order. */
+lce_status_t lce_forward_ex(const void* H, const void* W, const void* b, const int64_t* labels,
+                            const int32_t* valid_idx, int64_t C, int64_t N, int64_t D, int64_t V,
+                            lce_dtype_t dt, lce_reduction_t reduction, const float* loss_weights,
+                            double num_label_tokens, float* loss, float* m, float* logs, void* ws,
+                            size_t ws_bytes, void* stream);
+
+/* Backward pass for a chosen reduction (section 04 with the row factor of
+ * that reduction): G_ij = r_i (p_ij - 1[j = y_i]) on supervised rows, with
+ *   MEAN  r_i = lambda / C,  SUM  r_i = lambda w_i / n,  NONE  r_i = g_i,
+ * where lambda = grad_loss[0] (MEAN / SUM; NULL means 1) and g = grad_loss
+ * float[N] (NONE: the upstream gradient of each position's loss; NULL means
+ * 1 for every position).  reduction, loss_weights and num_label_tokens must
+ * be those of the forward call.  Outputs, determinism and the C == 0
+ * behaviour as in lce_backward. */
+lce_status_t lce_backward_ex(const void* H, const void* W, const void* b, const int64_t* labels,
+                             const int32_t* valid_idx, int64_t C, int64_t N, int64_t D, int64_t V,
+                             lce_dtype_t dt, lce_reduction_t reduction, const float* loss_weights,
+                             double num_label_tokens, const float* m, const float* logs,
+                             const float* grad_loss, void* dH, void* dW, void* db, void* ws,
+                             size_t ws_bytes, void* stream);
 
 /* Static string for a status code. */
 const char* lce_status_string(lce_status_t status);

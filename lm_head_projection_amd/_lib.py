@@ -25,12 +25,19 @@ LCE_ERR_WORKSPACE = -3
 LCE_ERR_HIP = -4
 LCE_ERR_UNSUPPORTED = -5
 
+LCE_REDUCTION_MEAN = 0
+LCE_REDUCTION_SUM = 1
+LCE_REDUCTION_NONE = 2
+REDUCTIONS = {"mean": LCE_REDUCTION_MEAN, "sum": LCE_REDUCTION_SUM, "none": LCE_REDUCTION_NONE}
+
 # Every entry point that include/lce.h declares.
 EXPORTS = (
     "lce_workspace_size",
     "lce_compact_valid",
     "lce_forward",
     "lce_backward",
+    "lce_forward_ex",
+    "lce_backward_ex",
     "lce_status_string",
     "lce_profile_start",
     "lce_profile_stop",
@@ -66,6 +73,13 @@ def load() -> ctypes.CDLL:
     lib.lce_backward.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
                                  vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.lce_backward.restype = ctypes.c_int
+    dbl = ctypes.c_double
+    lib.lce_forward_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
+                                   ctypes.c_int, vp, dbl, vp, vp, vp, vp, sz, vp]
+    lib.lce_forward_ex.restype = ctypes.c_int
+    lib.lce_backward_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
+                                    ctypes.c_int, vp, dbl, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.lce_backward_ex.restype = ctypes.c_int
     lib.lce_status_string.argtypes = [ctypes.c_int]
     lib.lce_status_string.restype = ctypes.c_char_p
     lib.lce_profile_start.argtypes = [i32]
@@ -133,6 +147,26 @@ def lce_backward(H, W, b, labels, valid_idx, C: int, m, logs, grad_loss, dH, dW,
     return load().lce_backward(_ptr(H), _ptr(W), _ptr(b), _ptr(labels), _ptr(valid_idx), C, N, D, V,
                                dtype_code(H.dtype), _ptr(m), _ptr(logs), _ptr(grad_loss), _ptr(dH),
                                _ptr(dW), _ptr(db), _ptr(ws), ws.numel(), _stream_ptr(stream))
+
+
+def lce_forward_ex(H, W, b, labels, valid_idx, C: int, reduction: int, loss_weights,
+                   num_label_tokens: float, loss, m, logs, ws, stream=None) -> int:
+    N, D = H.shape
+    V = W.shape[0]
+    return load().lce_forward_ex(_ptr(H), _ptr(W), _ptr(b), _ptr(labels), _ptr(valid_idx), C, N, D, V,
+                                 dtype_code(H.dtype), int(reduction), _ptr(loss_weights),
+                                 float(num_label_tokens), _ptr(loss), _ptr(m), _ptr(logs), _ptr(ws),
+                                 ws.numel(), _stream_ptr(stream))
+
+
+def lce_backward_ex(H, W, b, labels, valid_idx, C: int, reduction: int, loss_weights,
+                    num_label_tokens: float, m, logs, grad_loss, dH, dW, db, ws, stream=None) -> int:
+    N, D = H.shape
+    V = W.shape[0]
+    return load().lce_backward_ex(_ptr(H), _ptr(W), _ptr(b), _ptr(labels), _ptr(valid_idx), C, N, D, V,
+                                  dtype_code(H.dtype), int(reduction), _ptr(loss_weights),
+                                  float(num_label_tokens), _ptr(m), _ptr(logs), _ptr(grad_loss), _ptr(dH),
+                                  _ptr(dW), _ptr(db), _ptr(ws), ws.numel(), _stream_ptr(stream))
 
 
 def profile_start(max_launches: int = 65536) -> None:

@@ -12,6 +12,12 @@
 #include "lce.h"
 #include "lce_kernels.h"
 
+#include <cmath>
+
+static_assert(LCE_REDUCTION_MEAN == lce::kReduceMean && LCE_REDUCTION_SUM == lce::kReduceSum &&
+                  LCE_REDUCTION_NONE == lce::kReduceNone,
+              "reduction codes of the ABI and the kernels agree");
+
 using namespace lce;
 
 namespace {
@@ -82,6 +88,13 @@ template <typename T> struct Tile {
   static constexpr int BN = Cfg<T>::BN;  // row block
 };
 
+// A reduction of the per-row CE: mean over C, or sum_i w_i l_i / div, or none.
+struct Reduce {
+  int kind = kReduceMean;
+  const float* weights = nullptr;  // [N] per position (sum only) or null
+  double div = 1.0;                // sum only: the divisor (num_label_tokens, else 1)
+};
+
 struct Layout {
   // compaction
   size_t counts, bad, offsets, stat;
@@ -90,7 +103,7 @@ struct Layout {
   // forward
   size_t pm, ps, tgt, lrow;
   // backward
-  size_t mc, lsc, inv, G, slots, dbp;
+  size_t mc, lsc, rsc, inv, G, slots, dbp;
   size_t total;
   int64_t Npad, Vpad, Vc, nblk;
 };
@@ -127,6 +140,7 @@ bool make_layout(int64_t N, int64_t D, int64_t V, lce_dtype_t dt, Layout& L) {
   off = common_end;
   L.mc = take(L.Npad * 4);
   L.lsc = take(L.Npad * 4);
+  L.rsc = take(L.Npad * 4);
   L.inv = take(std::max<int64_t>(N, 1) * 4);
   L.G = take(L.Npad * L.Vc * esz);
   L.slots = take((int64_t)kDhSlotRows * L.Npad * D * 4);
@@ -246,8 +260,8 @@ lce_status_t fill_f32(float* p, int64_t n, float v, hipStream_t s) {
 template <typename T>
 lce_status_t forward_impl(const T* H, const T* W, const T* b, const int64_t* labels,
                           const int32_t* idx, int64_t C, int64_t N, int64_t D, int64_t V,
-                          float* loss, float* m, float* logs, float* row_loss, char* ws,
-                          const Layout& L, hipStream_t s) {
+                          const Reduce& red, float* loss, float* m, float* logs, float* row_loss,
+                          char* ws, const Layout& L, hipStream_t s) {
   using Cf = Cfg<T>;
   const int Cpad = (int)rup(C, 256);
   T* Hc = reinterpret_cast<T*>(ws + L.hc);
@@ -276,7 +290,9 @@ lce_status_t forward_impl(const T* H, const T* W, const T* b, const int64_t* lab
   LCE_TRY(fill_f32(row_loss, N, 0.f, s));
   LCE_LAUNCH("k_merge", k_merge, cdiv(C, 256), 256, 0, s, pm, ps, tgt, n_split, Cpad, (int)C, idx, m,
              logs, row_loss, lrow);
-  LCE_LAUNCH("k_loss_sum", k_loss_sum, 1, 1024, 0, s, lrow, (int)C, loss);
+  if (loss)
+    LCE_LAUNCH("k_loss_sum", k_loss_sum, 1, 1024, 0, s, lrow, (int)C, (int)red.kind, red.weights, idx,
+               red.div, loss);
   return LCE_OK;
 }
 
@@ -284,14 +300,15 @@ lce_status_t forward_impl(const T* H, const T* W, const T* b, const int64_t* lab
 template <typename T>
 lce_status_t backward_impl(const T* H, const T* W, const T* b, const int64_t* labels,
                            const int32_t* idx, int64_t C, int64_t N, int64_t D, int64_t V,
-                           const float* m, const float* logs, const float* grad_loss, T* dH, T* dW,
-                           T* db, char* ws, const Layout& L, hipStream_t s) {
+                           const Reduce& red, const float* m, const float* logs, const float* grad_loss,
+                           T* dH, T* dW, T* db, char* ws, const Layout& L, hipStream_t s) {
   using Cf = Cfg<T>;
   const int Cpad = (int)rup(C, 256);
   T* Hc = reinterpret_cast<T*>(ws + L.hc);
   int* yc = reinterpret_cast<int*>(ws + L.yc);
   float* mc = reinterpret_cast<float*>(ws + L.mc);
   float* lsc = reinterpret_cast<float*>(ws + L.lsc);
+  float* rsc = reinterpret_cast<float*>(ws + L.rsc);
   int* inv = reinterpret_cast<int*>(ws + L.inv);
   T* Gc = reinterpret_cast<T*>(ws + L.G);
   float* slots = reinterpret_cast<float*>(ws + L.slots);
@@ -310,6 +327,8 @@ lce_status_t backward_impl(const T* H, const T* W, const T* b, const int64_t* la
     const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(cdiv(N, 256), 4096));
     LCE_LAUNCH("k_fill_i32", k_fill_i32, grid, 256, 0, s, inv, N, -1);
     LCE_LAUNCH("k_inv_scatter", k_inv_scatter, cdiv(C, 256), 256, 0, s, idx, (int)C, inv);
+    LCE_LAUNCH("k_row_scale", k_row_scale, cdiv(Cpad, 256), 256, 0, s, idx, (int)C, Cpad, (int)red.kind,
+               red.weights, (float)red.div, grad_loss, rsc);
   }
   const int n_rb = Cpad / Cf::BN;
   const int n_nt = (int)cdiv(D, Cf::BN);
@@ -328,7 +347,7 @@ lce_status_t backward_impl(const T* H, const T* W, const T* b, const int64_t* la
       const int n_work = n_rb * (int)cdiv(vtiles, tpw);
       const int per_xcd = (int)cdiv(n_work, 8);
       LCE_LAUNCH("k_replay", (k_replay<T>), per_xcd * 8, kThreads, gemm_lds_bytes<T>(), s, W, b, Hc,
-                 yc, mc, lsc, Cpad, (int)D, (int)V, (int)v0, vtiles, tpw, n_rb, n_work, per_xcd, Gc, ldg,
+                 yc, mc, lsc, rsc, Cpad, (int)D, (int)V, (int)v0, vtiles, tpw, n_rb, n_work, per_xcd, Gc, ldg,
                  db ? dbp : (float*)nullptr, lddb);
     }
     // K5: dH split so that one dH tile's K matches one dW tile's K (= Cpad).
@@ -342,18 +361,17 @@ lce_status_t backward_impl(const T* H, const T* W, const T* b, const int64_t* la
     const int dh_first = ks_len >= Cpad ? 1 : 0;
     LCE_LAUNCH("k_grad", (k_grad<T>), per_xcd * 8, kThreads, gemm_lds_bytes<T>(), s, Gc, ldg, kpad, Hc,
                W, Cpad, (int)D, (int)v0, vc, (int)(V - v0), n_nt, n_dh_mt, (int)ks_len, n_dh, vtiles,
-               dh_first, slots, slot_stride, chunk == 0 ? 0 : 1, dW, grad_loss, (int)C);
+               dh_first, slots, slot_stride, chunk == 0 ? 0 : 1, dW);
   }
   {
     const int64_t vec = N * (D / 4);
     const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(cdiv(vec, 256), 8192));
     LCE_LAUNCH("k_dh_finalize", (k_dh_finalize<T>), grid, 256, 0, s, slots, S, slot_stride, inv, N,
-               (int)D, grad_loss, (int)C, dH);
+               (int)D, dH);
   }
   if (db) {
     const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(cdiv(V, 256), 4096));
-    LCE_LAUNCH("k_db_finalize", (k_db_finalize<T>), grid, 256, 0, s, dbp, n_rb, lddb, (int)V,
-               grad_loss, (int)C, db);
+    LCE_LAUNCH("k_db_finalize", (k_db_finalize<T>), grid, 256, 0, s, dbp, n_rb, lddb, (int)V, db);
   }
   return LCE_OK;
 }
@@ -370,6 +388,86 @@ lce_status_t shape_supported(int64_t N, int64_t D, int64_t V, lce_dtype_t dt) {
   if (N > (int64_t)1 << 30 || V > (int64_t)1 << 30 || D > (int64_t)1 << 20) return LCE_ERR_UNSUPPORTED;
   if (N * D > ((int64_t)1 << 40) || V * D > ((int64_t)1 << 40)) return LCE_ERR_UNSUPPORTED;
   return LCE_OK;
+}
+
+lce_status_t make_reduce(int kind, const float* weights, double num, Reduce& r) {
+  if (kind != kReduceMean && kind != kReduceSum && kind != kReduceNone) return LCE_ERR_ARG;
+  if (!(num >= 0.0) || std::isinf(num)) return LCE_ERR_ARG;  // also rejects NaN
+  if (kind != kReduceSum && (weights != nullptr || num != 0.0)) return LCE_ERR_ARG;
+  r.kind = kind;
+  r.weights = weights;
+  r.div = num > 0.0 ? num : 1.0;
+  return LCE_OK;
+}
+
+// Shared by lce_forward and lce_forward_ex.  `loss` (scalar) and `row_loss`
+// ([N]) are each optional; m and logs may be null (no backward follows).
+lce_status_t forward_entry(const void* H, const void* W, const void* b, const int64_t* labels,
+                           const int32_t* valid_idx, int64_t C, int64_t N, int64_t D, int64_t V,
+                           lce_dtype_t dt, const Reduce& red, float* loss, float* m, float* logs,
+                           float* row_loss, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    if (!dims_ok(N, D, V, dt) || C < 0 || C > N) return LCE_ERR_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (C == 0) {
+      if (loss) LCE_LAUNCH("k_store_scalar", k_store_scalar, 1, 1, 0, s, loss, 0.f);
+      LCE_TRY(fill_f32(m, N, -INFINITY, s));
+      LCE_TRY(fill_f32(logs, N, -INFINITY, s));
+      LCE_TRY(fill_f32(row_loss, N, 0.f, s));
+      return LCE_OK_EMPTY;
+    }
+    if (!H || !W || !labels || !valid_idx || !ws) return LCE_ERR_ARG;
+    if (!aligned16(H) || !aligned16(W) || !aligned16(ws)) return LCE_ERR_ARG;
+    LCE_TRY(shape_supported(N, D, V, dt));
+    Layout L;
+    if (!make_layout(N, D, V, dt, L)) return LCE_ERR_ARG;
+    if (ws_bytes < L.total) return LCE_ERR_WORKSPACE;
+    char* w = static_cast<char*>(ws);
+    if (dt == LCE_DTYPE_BF16)
+      return forward_impl<uint16_t>((const uint16_t*)H, (const uint16_t*)W, (const uint16_t*)b, labels,
+                                    valid_idx, C, N, D, V, red, loss, m, logs, row_loss, w, L, s);
+    return forward_impl<float>((const float*)H, (const float*)W, (const float*)b, labels, valid_idx, C,
+                               N, D, V, red, loss, m, logs, row_loss, w, L, s);
+  } catch (...) {
+    return LCE_ERR_HIP;
+  }
+}
+
+// Shared by lce_backward and lce_backward_ex.
+lce_status_t backward_entry(const void* H, const void* W, const void* b, const int64_t* labels,
+                            const int32_t* valid_idx, int64_t C, int64_t N, int64_t D, int64_t V,
+                            lce_dtype_t dt, const Reduce& red, const float* m, const float* logs,
+                            const float* grad_loss, void* dH, void* dW, void* db, void* ws,
+                            size_t ws_bytes, void* stream) {
+  try {
+    if (!dims_ok(N, D, V, dt) || C < 0 || C > N) return LCE_ERR_ARG;
+    if (!dW || (N > 0 && !dH)) return LCE_ERR_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t esz = dt == LCE_DTYPE_BF16 ? 2 : 4;
+    if (C == 0) {
+      LCE_TRY(zero_bytes(dH, N * D * esz, s));
+      LCE_TRY(zero_bytes(dW, V * D * esz, s));
+      LCE_TRY(zero_bytes(db, V * esz, s));
+      return LCE_OK_EMPTY;
+    }
+    if (!H || !W || !labels || !valid_idx || !m || !logs || !ws) return LCE_ERR_ARG;
+    if (!aligned16(H) || !aligned16(W) || !aligned16(ws) || !aligned16(dH) || !aligned16(dW))
+      return LCE_ERR_ARG;
+    LCE_TRY(shape_supported(N, D, V, dt));
+    Layout L;
+    if (!make_layout(N, D, V, dt, L)) return LCE_ERR_ARG;
+    if (ws_bytes < L.total) return LCE_ERR_WORKSPACE;
+    char* w = static_cast<char*>(ws);
+    if (dt == LCE_DTYPE_BF16)
+      return backward_impl<uint16_t>((const uint16_t*)H, (const uint16_t*)W, (const uint16_t*)b, labels,
+                                     valid_idx, C, N, D, V, red, m, logs, grad_loss, (uint16_t*)dH,
+                                     (uint16_t*)dW, (uint16_t*)db, w, L, s);
+    return backward_impl<float>((const float*)H, (const float*)W, (const float*)b, labels, valid_idx, C,
+                                N, D, V, red, m, logs, grad_loss, (float*)dH, (float*)dW, (float*)db, w,
+                                L, s);
+  } catch (...) {
+    return LCE_ERR_HIP;
+  }
 }
 
 }  // namespace
@@ -438,67 +536,44 @@ lce_status_t lce_forward(const void* H, const void* W, const void* b, const int6
                          const int32_t* valid_idx, int64_t C, int64_t N, int64_t D, int64_t V,
                          lce_dtype_t dt, float* loss, float* m, float* logs, float* row_loss,
                          void* ws, size_t ws_bytes, void* stream) {
-  try {
-    if (!dims_ok(N, D, V, dt) || C < 0 || C > N) return LCE_ERR_ARG;
-    if (!loss || (N > 0 && (!m || !logs))) return LCE_ERR_ARG;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (C == 0) {
-      LCE_LAUNCH("k_store_scalar", k_store_scalar, 1, 1, 0, s, loss, 0.f);
-      LCE_TRY(fill_f32(m, N, -INFINITY, s));
-      LCE_TRY(fill_f32(logs, N, -INFINITY, s));
-      LCE_TRY(fill_f32(row_loss, N, 0.f, s));
-      return LCE_OK_EMPTY;
-    }
-    if (!H || !W || !labels || !valid_idx || !ws) return LCE_ERR_ARG;
-    if (!aligned16(H) || !aligned16(W) || !aligned16(ws)) return LCE_ERR_ARG;
-    LCE_TRY(shape_supported(N, D, V, dt));
-    Layout L;
-    if (!make_layout(N, D, V, dt, L)) return LCE_ERR_ARG;
-    if (ws_bytes < L.total) return LCE_ERR_WORKSPACE;
-    char* w = static_cast<char*>(ws);
-    if (dt == LCE_DTYPE_BF16)
-      return forward_impl<uint16_t>((const uint16_t*)H, (const uint16_t*)W, (const uint16_t*)b, labels,
-                                    valid_idx, C, N, D, V, loss, m, logs, row_loss, w, L, s);
-    return forward_impl<float>((const float*)H, (const float*)W, (const float*)b, labels, valid_idx, C,
-                               N, D, V, loss, m, logs, row_loss, w, L, s);
-  } catch (...) {
-    return LCE_ERR_HIP;
-  }
+  if (!loss || (N > 0 && (!m || !logs))) return LCE_ERR_ARG;
+  return forward_entry(H, W, b, labels, valid_idx, C, N, D, V, dt, Reduce{}, loss, m, logs, row_loss, ws,
+                       ws_bytes, stream);
+}
+
+lce_status_t lce_forward_ex(const void* H, const void* W, const void* b, const int64_t* labels,
+                            const int32_t* valid_idx, int64_t C, int64_t N, int64_t D, int64_t V,
+                            lce_dtype_t dt, lce_reduction_t reduction, const float* loss_weights,
+                            double num_label_tokens, float* loss, float* m, float* logs, void* ws,
+                            size_t ws_bytes, void* stream) {
+  Reduce red;
+  LCE_TRY(make_reduce(reduction, loss_weights, num_label_tokens, red));
+  if (!loss) return LCE_ERR_ARG;
+  if (red.kind == kReduceNone)  // per-position losses: loss is float[N]
+    return forward_entry(H, W, b, labels, valid_idx, C, N, D, V, dt, red, nullptr, m, logs, loss, ws,
+                         ws_bytes, stream);
+  return forward_entry(H, W, b, labels, valid_idx, C, N, D, V, dt, red, loss, m, logs, nullptr, ws,
+                       ws_bytes, stream);
 }
 
 lce_status_t lce_backward(const void* H, const void* W, const void* b, const int64_t* labels,
                           const int32_t* valid_idx, int64_t C, int64_t N, int64_t D, int64_t V,
                           lce_dtype_t dt, const float* m, const float* logs, const float* grad_loss,
                           void* dH, void* dW, void* db, void* ws, size_t ws_bytes, void* stream) {
-  try {
-    if (!dims_ok(N, D, V, dt) || C < 0 || C > N) return LCE_ERR_ARG;
-    if (!dW || (N > 0 && !dH)) return LCE_ERR_ARG;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const int64_t esz = dt == LCE_DTYPE_BF16 ? 2 : 4;
-    if (C == 0) {
-      LCE_TRY(zero_bytes(dH, N * D * esz, s));
-      LCE_TRY(zero_bytes(dW, V * D * esz, s));
-      LCE_TRY(zero_bytes(db, V * esz, s));
-      return LCE_OK_EMPTY;
-    }
-    if (!H || !W || !labels || !valid_idx || !m || !logs || !ws) return LCE_ERR_ARG;
-    if (!aligned16(H) || !aligned16(W) || !aligned16(ws) || !aligned16(dH) || !aligned16(dW))
-      return LCE_ERR_ARG;
-    LCE_TRY(shape_supported(N, D, V, dt));
-    Layout L;
-    if (!make_layout(N, D, V, dt, L)) return LCE_ERR_ARG;
-    if (ws_bytes < L.total) return LCE_ERR_WORKSPACE;
-    char* w = static_cast<char*>(ws);
-    if (dt == LCE_DTYPE_BF16)
-      return backward_impl<uint16_t>((const uint16_t*)H, (const uint16_t*)W, (const uint16_t*)b, labels,
-                                     valid_idx, C, N, D, V, m, logs, grad_loss, (uint16_t*)dH,
-                                     (uint16_t*)dW, (uint16_t*)db, w, L, s);
-    return backward_impl<float>((const float*)H, (const float*)W, (const float*)b, labels, valid_idx, C,
-                                N, D, V, m, logs, grad_loss, (float*)dH, (float*)dW, (float*)db, w, L,
-                                s);
-  } catch (...) {
-    return LCE_ERR_HIP;
-  }
+  return backward_entry(H, W, b, labels, valid_idx, C, N, D, V, dt, Reduce{}, m, logs, grad_loss, dH, dW,
+                        db, ws, ws_bytes, stream);
+}
+
+lce_status_t lce_backward_ex(const void* H, const void* W, const void* b, const int64_t* labels,
+                             const int32_t* valid_idx, int64_t C, int64_t N, int64_t D, int64_t V,
+                             lce_dtype_t dt, lce_reduction_t reduction, const float* loss_weights,
+                             double num_label_tokens, const float* m, const float* logs,
+                             const float* grad_loss, void* dH, void* dW, void* db, void* ws,
+                             size_t ws_bytes, void* stream) {
+  Reduce red;
+  LCE_TRY(make_reduce(reduction, loss_weights, num_label_tokens, red));
+  return backward_entry(H, W, b, labels, valid_idx, C, N, D, V, dt, red, m, logs, grad_loss, dH, dW, db, ws,
+                        ws_bytes, stream);
 }
 
 lce_status_t lce_profile_start(int32_t max_launches) {

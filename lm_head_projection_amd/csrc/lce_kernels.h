@@ -6,7 +6,8 @@
 //   K3  k_merge / k_loss_sum                       split merge, per-row CE, mean
 //   K4  k_replay                                   score tiles -> G = p - onehot
 //   K5  k_grad                                     dH (+= G W) and dW (= G^T Hc)
-//   K6  k_dh_finalize / k_db_finalize              ordered sums, lambda/C, cast
+//   K6  k_dh_finalize / k_db_finalize              ordered sums, cast
+//   k_row_scale                                    per-row factor r_c of G
 //
 // Page references are to "分块交叉熵：从输出投影开始省保存量" (glenzli.com):
 // section 01 (objective, tile steps), section 02 (running LSE), section 04
@@ -400,25 +401,56 @@ __global__ __launch_bounds__(256) void k_merge(const float* __restrict__ pm, con
   const float ls = logf(s);
   const float l = (m - tgt[c]) + ls;
   const int n = idx[c];
-  m_out[n] = m;
-  logs_out[n] = ls;
+  if (m_out) m_out[n] = m;
+  if (logs_out) logs_out[n] = ls;
   if (row_loss) row_loss[n] = l;
   lrow[c] = l;
 }
 
-// loss = (1/C) sum_c l_c, summed in float64 in a fixed order.
+// Reductions of the per-row CE (NeMo chunked_ce page, ChunkedCrossEntropy.forward:
+// mean over the supervised rows, or a sum with optional per-position weights
+// divided by an external token count), summed in float64 in a fixed order:
+//   mean: loss = (1/C) sum_c l_c
+//   sum:  loss = (sum_c w_{idx_c} l_c) / div     (w = 1 without weights)
+constexpr int kReduceMean = 0, kReduceSum = 1, kReduceNone = 2;
+
 __global__ __launch_bounds__(1024) void k_loss_sum(const float* __restrict__ lrow, int C,
+                                                   int reduction, const float* __restrict__ weights,
+                                                   const int32_t* __restrict__ idx, double div,
                                                    float* __restrict__ loss) {
   __shared__ double s[1024];
   double acc = 0.0;
-  for (int c = threadIdx.x; c < C; c += 1024) acc += (double)lrow[c];
+  for (int c = threadIdx.x; c < C; c += 1024)
+    acc += weights ? (double)weights[idx[c]] * (double)lrow[c] : (double)lrow[c];
   s[threadIdx.x] = acc;
   __syncthreads();
   for (int off = 512; off > 0; off >>= 1) {
     if (threadIdx.x < off) s[threadIdx.x] += s[threadIdx.x + off];
     __syncthreads();
   }
-  if (threadIdx.x == 0) loss[0] = (float)(s[0] / (double)C);
+  if (threadIdx.x == 0) loss[0] = (float)(reduction == kReduceMean ? s[0] / (double)C : s[0] / div);
+}
+
+// r_c, the factor of row c's (p - onehot) in G (section 04: lambda a_i / C for
+// the mean; the derivative of the chosen reduction otherwise):
+//   mean: lambda / C;  sum: lambda w_{idx_c} / div;  none: g_{idx_c} (per-row
+//   upstream gradient).  lambda = grad[0] (1 without grad).  Padding rows: 0.
+__global__ void k_row_scale(const int32_t* __restrict__ idx, int C, int Cpad, int reduction,
+                            const float* __restrict__ weights, float div, const float* __restrict__ grad,
+                            float* __restrict__ rsc) {
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= Cpad) return;
+  float r = 0.f;
+  if (c < C) {
+    const int n = idx[c];
+    if (reduction == kReduceNone) {
+      r = grad ? grad[n] : 1.f;
+    } else {
+      const float lam = grad ? grad[0] : 1.f;
+      r = reduction == kReduceMean ? lam / (float)C : lam * (weights ? weights[n] : 1.f) / div;
+    }
+  }
+  rsc[c] = r;
 }
 
 __global__ void k_fill_f32(float* __restrict__ p, int64_t n, float v) {
@@ -444,15 +476,16 @@ __global__ void k_store_scalar(float* __restrict__ p, float v) { p[0] = v; }
 // ============================================================== K4 replay
 // Work item = (row block, run of `tpw` vocabulary tiles of this chunk).  For
 // each tile: recompute the score tile, p = exp((Z - m) - log s) from the
-// saved statistics, subtract 1 at the target column (global id), write
-// G = p - onehot (unscaled; lambda/C is applied in the gradient epilogues)
-// into the chunk buffer G[c][v - v0], and, with a bias, the per-row-block
-// column sums of G (db partials) in a fixed order.
+// saved statistics, subtract 1 at the target column (global id), scale row c
+// by its factor r_c (k_row_scale), write G = r_c (p - onehot) into the chunk
+// buffer, and, with a bias, the per-row-block column sums of G (db partials)
+// in a fixed order.
 template <typename T>
 __device__ __forceinline__ void replay_epilogue(f32x16_t (&acc)[Geo<T>::TM][Geo<T>::TN],
                                                 const T* __restrict__ bias, int m0, int n0, int V, int v0,
                                                 const int* __restrict__ yc, const float* __restrict__ mc,
-                                                const float* __restrict__ lsc, T* __restrict__ Gc,
+                                                const float* __restrict__ lsc, const float* __restrict__ rsc,
+                                                T* __restrict__ Gc,
                                                 int64_t ldg, float* __restrict__ dbp, int64_t lddb,
                                                 int rb, float* red, bool raw_sync,
                                                 const uint16_t* bias_slice = nullptr) {
@@ -469,24 +502,38 @@ __device__ __forceinline__ void replay_epilogue(f32x16_t (&acc)[Geo<T>::TM][Geo<
   } else {
     if (bias) add_bias<T>(acc, bias, vbase, V, lane);
   }
+  // bf16: the sign of r_c is applied when G is packed (sign bits of a bf16
+  // pair) and in the db sums; the exponent carries |r_c|.
+  uint32_t smask[G::TN];
+  float sgn[G::TN];
 #pragma unroll
   for (int tn = 0; tn < G::TN; ++tn) {
     const int r = n0 + wn * G::WTN + tn * 32 + (lane & 31);
     // p = exp((Z - m) - log s) from the saved statistics (section 04).
-    const float mr = mc[r], lr = lsc[r];
+    const float mr = mc[r], lr = lsc[r], rr = rsc[r];
+    float sub;  // r_c at the target column
     if constexpr (sizeof(T) == 4) {
 #pragma unroll
       for (int tm = 0; tm < G::TM; ++tm)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          acc[tm][tn][i] = __builtin_amdgcn_exp2f(((acc[tm][tn][i] - mr) - lr) * kLog2e);
+          acc[tm][tn][i] = rr * __builtin_amdgcn_exp2f(((acc[tm][tn][i] - mr) - lr) * kLog2e);
+      sub = rr;
+      smask[tn] = 0u;
+      sgn[tn] = 1.f;
     } else {
-      const float ml = mr * kLog2e, ll = lr * kLog2e;
+      // |r| p = exp2(Z log2e - m log2e - (log s log2e - log2 |r|)); r = 0 gives 0.
+      const float ar = fabsf(rr);
+      const float ml = mr * kLog2e, ll = lr * kLog2e - log2f(ar);
 #pragma unroll
       for (int tm = 0; tm < G::TM; ++tm)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
           acc[tm][tn][i] = __builtin_amdgcn_exp2f(fmaf(acc[tm][tn][i], kLog2e, -ml) - ll);
+      sub = ar;
+      const bool neg = (__float_as_uint(rr) >> 31) != 0u;
+      smask[tn] = neg ? 0x80008000u : 0u;
+      sgn[tn] = neg ? -1.f : 1.f;
     }
     const int d = yc[r] - vbase;
     if ((unsigned)d < (unsigned)G::WTM) {
@@ -494,7 +541,7 @@ __device__ __forceinline__ void replay_epilogue(f32x16_t (&acc)[Geo<T>::TM][Geo<
       for (int tm = 0; tm < G::TM; ++tm)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          if (acc_row(tm, i, lane) == d) acc[tm][tn][i] -= 1.f;
+          if (acc_row(tm, i, lane) == d) acc[tm][tn][i] -= sub;
     }
   }
   if (m0 + C::BM > V) {
@@ -524,8 +571,9 @@ __device__ __forceinline__ void replay_epilogue(f32x16_t (&acc)[Geo<T>::TM][Geo<
         uint32_t d[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k)
-          d[k] = (uint32_t)from_f32<uint16_t>(acc[tm][tn][2 * k]) |
-                 ((uint32_t)from_f32<uint16_t>(acc[tm][tn][2 * k + 1]) << 16);
+          d[k] = ((uint32_t)from_f32<uint16_t>(acc[tm][tn][2 * k]) |
+                  ((uint32_t)from_f32<uint16_t>(acc[tm][tn][2 * k + 1]) << 16)) ^
+                 smask[tn];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           // lanes 32..63 of d[k] <-> lanes 0..31 of d[k + 4]
@@ -563,7 +611,7 @@ __device__ __forceinline__ void replay_epilogue(f32x16_t (&acc)[Geo<T>::TM][Geo<
     for (int i = 0; i < 16; ++i) {
       float sum = 0.f;
 #pragma unroll
-      for (int tn = 0; tn < G::TN; ++tn) sum += acc[tm][tn][i];
+      for (int tn = 0; tn < G::TN; ++tn) sum = fmaf(sgn[tn], acc[tm][tn][i], sum);
       cs[tm * 16 + i] = sum;
     }
   halfwave_reduce_scatter<NV>(cs, lane);
@@ -593,7 +641,8 @@ __device__ __forceinline__ void replay_epilogue(f32x16_t (&acc)[Geo<T>::TM][Geo<
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k_replay(
     const T* __restrict__ W, const T* __restrict__ bias, const T* __restrict__ Hc,
-    const int* __restrict__ yc, const float* __restrict__ mc, const float* __restrict__ lsc, int Cpad,
+    const int* __restrict__ yc, const float* __restrict__ mc, const float* __restrict__ lsc,
+    const float* __restrict__ rsc, int Cpad,
     int D, int V, int v0, int vtiles, int tpw, int n_rb, int n_work, int per_xcd, T* __restrict__ Gc,
     int64_t ldg, float* __restrict__ dbp, int64_t lddb) {
   using C = Cfg<T>;
@@ -620,7 +669,7 @@ __global__ __launch_bounds__(kThreads) void k_replay(
           k0 = 0;
         },
         [&](int t, f32x16_t (&acc)[G::TM][G::TN]) {
-          replay_epilogue<T>(acc, bias, v0 + (vt0 + t) * C::BM, n0, V, v0, yc, mc, lsc, Gc, ldg, dbp, lddb,
+          replay_epilogue<T>(acc, bias, v0 + (vt0 + t) * C::BM, n0, V, v0, yc, mc, lsc, rsc, Gc, ldg, dbp, lddb,
                              rb, red, true, pipe::bias_slice(smem_raw, t));
         },
         true, reinterpret_cast<const uint16_t*>(bias), V);
@@ -632,7 +681,7 @@ __global__ __launch_bounds__(kThreads) void k_replay(
       zero_acc<T>(acc);
       gemm_tile<T, true, true>(W, (int64_t)V * D, D, m0, Hc, (int64_t)Cpad * D, D, n0, 0, D, nsteps, acc,
                                smem);
-      replay_epilogue<T>(acc, bias, m0, n0, V, v0, yc, mc, lsc, Gc, ldg, dbp, lddb, rb,
+      replay_epilogue<T>(acc, bias, m0, n0, V, v0, yc, mc, lsc, rsc, Gc, ldg, dbp, lddb, rb,
                          reinterpret_cast<float*>(smem_raw), false);
       __syncthreads();  // the next tile's loads reuse the LDS the db sums used
     }
@@ -645,15 +694,15 @@ __global__ __launch_bounds__(kThreads) void k_replay(
 //    G[c][v] W[v0+v][d]  (dH_T += G_{T,B} W_B, section 04).  The chunk's
 //    vocabulary range is cut into S splits; slot ks accumulates split ks of
 //    every chunk in chunk order (stream order), so the sum is deterministic.
-//  * dW tiles: dW[v0+v][d] = (lambda/C) sum_c G[c][v] Hc[c][d]
+//  * dW tiles: dW[v0+v][d] = sum_c G[c][v] Hc[c][d]
 //    (dW_B += G^T H_T summed over every row block inside one tile, so each dW
-//    row is written exactly once).
+//    row is written exactly once).  G already carries the row factors r_c.
 // Operands: G is K-contiguous for dH (k = v) and K-outer for dW (k = c); W
-// (k = v) and Hc (k = c) are K-outer; the loaders transpose them in registers.
+// (k = v) and Hc (k = c) are K-outer (read with transposing LDS reads).
 template <typename T>
 __device__ __forceinline__ void grad_store(const f32x16_t (&acc)[Geo<T>::TM][Geo<T>::TN], bool dh, int m0,
                                            int n0, int D, int vc, int v0, float* slot, int accumulate,
-                                           T* __restrict__ dW, float scale) {
+                                           T* __restrict__ dW) {
   using G = Geo<T>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave % G::WGM, wn = wave / G::WGM;
@@ -670,7 +719,7 @@ __device__ __forceinline__ void grad_store(const f32x16_t (&acc)[Geo<T>::TM][Geo
           float* p = slot + (int64_t)r * D + n;
           *p = accumulate ? (*p + acc[tm][tn][i]) : acc[tm][tn][i];
         } else if (r < vc) {
-          dW[(int64_t)(v0 + r) * D + n] = from_f32<T>(scale * acc[tm][tn][i]);
+          dW[(int64_t)(v0 + r) * D + n] = from_f32<T>(acc[tm][tn][i]);
         }
       }
       // One 32x32 block at a time keeps the read-modify-write registers bounded.
@@ -684,7 +733,7 @@ __global__ __launch_bounds__(kThreads) void k_grad(
     const T* __restrict__ Gc, int64_t ldg, int kpad_g, const T* __restrict__ Hc,
     const T* __restrict__ W, int Cpad, int D, int v0, int vc, int w_rows, int n_nt, int n_dh_mt, int ks_len,
     int n_dh, int n_dw_mt, int dh_first, float* __restrict__ slots, int64_t slot_stride,
-    int accumulate, T* __restrict__ dW, const float* __restrict__ grad_loss, int Ctrue) {
+    int accumulate, T* __restrict__ dW) {
   using C = Cfg<T>;
   using G = Geo<T>;
   extern __shared__ __align__(16) char smem_raw[];
@@ -726,7 +775,6 @@ __global__ __launch_bounds__(kThreads) void k_grad(
     kb = 0;
     nsteps = Cpad / C::BK;
   }
-  const float scale = (grad_loss ? grad_loss[0] : 1.f) / (float)Ctrue;
   if constexpr (sizeof(T) == 2) {
     // dH_T += G_T,B W_B: A = G (k = v contiguous), B = W rows (k-outer).
     // dW_B = G^T Hc: A = G (k = c outer), B = Hc (k-outer).
@@ -749,7 +797,7 @@ __global__ __launch_bounds__(kThreads) void k_grad(
       pipe::run<0, false>(1, nsteps, nsteps * C::BK, smem_raw, acc, origin, no_epi);
     else
       pipe::run<1, false>(1, nsteps, nsteps * C::BK, smem_raw, acc, origin, no_epi);
-    grad_store<T>(acc, dh, m0, n0, D, vc, v0, slot, accumulate, dW, scale);
+    grad_store<T>(acc, dh, m0, n0, D, vc, v0, slot, accumulate, dW);
   } else {
     T* smem = reinterpret_cast<T*>(smem_raw);
     f32x16_t acc[G::TM][G::TN];
@@ -762,17 +810,16 @@ __global__ __launch_bounds__(kThreads) void k_grad(
       gemm_tile<T, false, false>(Gc, (int64_t)Cpad * ldg, ldg, m0, Hc, (int64_t)Cpad * D, D, n0, 0, Cpad,
                                  nsteps, acc, smem);
     }
-    grad_store<T>(acc, dh, m0, n0, D, vc, v0, slot, accumulate, dW, scale);
+    grad_store<T>(acc, dh, m0, n0, D, vc, v0, slot, accumulate, dW);
   }
 }
 
 // ============================================================== K6 finalize
-// dH[n] = (lambda/C) sum_ks slot[ks][inv[n]] for supervised rows, 0 otherwise.
+// dH[n] = sum_ks slot[ks][inv[n]] for supervised rows (G already carries the
+// row factors), 0 otherwise.
 template <typename T>
 __global__ void k_dh_finalize(const float* __restrict__ slots, int S, int64_t slot_stride,
-                              const int* __restrict__ inv, int64_t N, int D,
-                              const float* __restrict__ grad_loss, int Ctrue, T* __restrict__ dH) {
-  const float scale = (grad_loss ? grad_loss[0] : 1.f) / (float)Ctrue;
+                              const int* __restrict__ inv, int64_t N, int D, T* __restrict__ dH) {
   const int vpr = D / 4;
   const int64_t total = N * vpr;
   for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total;
@@ -789,23 +836,20 @@ __global__ void k_dh_finalize(const float* __restrict__ slots, int S, int64_t sl
         o[2] += v[2];
         o[3] += v[3];
       }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) o[j] *= scale;
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) dH[n * D + d + j] = from_f32<T>(o[j]);
   }
 }
 
-// db[v] = (lambda/C) sum_rb dbp[rb][v] in row-block order.
+// db[v] = sum_rb dbp[rb][v] in row-block order.
 template <typename T>
 __global__ void k_db_finalize(const float* __restrict__ dbp, int n_rb, int64_t lddb, int V,
-                              const float* __restrict__ grad_loss, int Ctrue, T* __restrict__ db) {
-  const float scale = (grad_loss ? grad_loss[0] : 1.f) / (float)Ctrue;
+                              T* __restrict__ db) {
   for (int v = blockIdx.x * blockDim.x + threadIdx.x; v < V; v += gridDim.x * blockDim.x) {
     float s = 0.f;
     for (int rb = 0; rb < n_rb; ++rb) s += dbp[(int64_t)rb * lddb + v];
-    db[v] = from_f32<T>(scale * s);
+    db[v] = from_f32<T>(s);
   }
 }
 

@@ -41,23 +41,28 @@ def _check(st: int, where: str, allow_empty: bool = True):
 
 class LinearCrossEntropyFunction(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, H, W, b, labels, mask, ignore_index):
+    def forward(ctx, H, W, b, labels, mask, ignore_index, reduction, loss_weights, num_label_tokens):
         H = H.contiguous()
         W = W.contiguous()
         b = None if b is None else b.contiguous()
         labels = labels.contiguous().to(torch.int64)
         if W.dtype != H.dtype or (b is not None and b.dtype != H.dtype):
             raise TypeError("H, W and b must share one dtype")
+        red = _lib.REDUCTIONS[reduction]
+        w = None if loss_weights is None else loss_weights.to(torch.float32).contiguous()
+        num = 0.0 if num_label_tokens is None else float(num_label_tokens)
         s = Saved(H, W, b, labels, mask, ignore_index)
         st, C = _lib.lce_compact_valid(labels, s.mask_u8, s.V, ignore_index, s.valid_idx, s.ws)
         _check(st, "lce_compact_valid")
         s.C = C
-        st = _lib.lce_forward(H, W, b, labels, s.valid_idx, C, s.loss, s.m, s.logs, None, s.ws)
-        _check(st, "lce_forward")
+        out = torch.empty(s.N if red == _lib.LCE_REDUCTION_NONE else 1, dtype=torch.float32, device=H.device)
+        st = _lib.lce_forward_ex(H, W, b, labels, s.valid_idx, C, red, w, num, out, s.m, s.logs, s.ws)
+        _check(st, "lce_forward_ex")
         ctx.s = s
+        ctx.red, ctx.w, ctx.num = red, w, num
         ctx.save_for_backward(H, W, b, labels)
         ctx.has_bias = b is not None
-        return s.loss[0].clone()
+        return out.clone() if red == _lib.LCE_REDUCTION_NONE else out[0].clone()
 
     @staticmethod
     def backward(ctx, grad):
@@ -66,24 +71,37 @@ class LinearCrossEntropyFunction(torch.autograd.Function):
         dH = torch.empty_like(H)
         dW = torch.empty_like(W)
         db = torch.empty_like(b) if ctx.has_bias else None
-        g = grad.reshape(1).to(torch.float32).contiguous()
-        st = _lib.lce_backward(H, W, b, labels, s.valid_idx, s.C, s.m, s.logs, g, dH, dW, db, s.ws)
-        _check(st, "lce_backward")
-        return dH, dW, db, None, None, None
+        g = grad.reshape(-1).to(torch.float32).contiguous()
+        st = _lib.lce_backward_ex(H, W, b, labels, s.valid_idx, s.C, ctx.red, ctx.w, ctx.num, s.m, s.logs,
+                                  g, dH, dW, db, s.ws)
+        _check(st, "lce_backward_ex")
+        return dH, dW, db, None, None, None, None, None, None
 
 
 def linear_cross_entropy(hidden: torch.Tensor, weight: torch.Tensor, labels: torch.Tensor,
                          bias: Optional[torch.Tensor] = None, mask: Optional[torch.Tensor] = None,
-                         ignore_index: int = IGNORE_INDEX) -> torch.Tensor:
-    """Mean CE over supervised rows of (hidden @ weight.T + bias) without forming the logits.
+                         ignore_index: int = IGNORE_INDEX, reduction: str = "mean",
+                         loss_weights: Optional[torch.Tensor] = None,
+                         num_label_tokens: Optional[float] = None) -> torch.Tensor:
+    """CE of (hidden @ weight.T + bias) over supervised rows without forming the logits.
 
     hidden [N, D], weight [V, D], bias [V] (optional), labels [N] (int),
-    mask [N] (optional bool; False = unsupervised).  Returns an fp32 scalar;
-    with no supervised rows it returns 0 and every gradient is exactly 0.
+    mask [N] (optional bool; False = unsupervised).
+    reduction "mean" (over the supervised rows), "sum" (optionally weighted by
+    loss_weights [N] and divided by num_label_tokens) or "none" (per-position
+    losses [N], 0 on unsupervised positions).  With no supervised rows the
+    loss is 0 and every gradient is exactly 0.
     """
     if hidden.dim() != 2:
+        lead = labels.shape
         hidden = hidden.reshape(-1, hidden.shape[-1])
         labels = labels.reshape(-1)
         if mask is not None:
             mask = mask.reshape(-1)
-    return LinearCrossEntropyFunction.apply(hidden, weight, bias, labels, mask, ignore_index)
+        if loss_weights is not None:
+            loss_weights = loss_weights.reshape(-1)
+        out = LinearCrossEntropyFunction.apply(hidden, weight, bias, labels, mask, ignore_index, reduction,
+                                               loss_weights, num_label_tokens)
+        return out.reshape(lead) if reduction == "none" else out
+    return LinearCrossEntropyFunction.apply(hidden, weight, bias, labels, mask, ignore_index, reduction,
+                                           loss_weights, num_label_tokens)

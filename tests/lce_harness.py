@@ -109,3 +109,57 @@ def assert_stat_close(name, x, ref, r):
     bound = r * np.maximum(1.0, np.abs(ref))
     bad = np.abs(x - ref) > bound
     assert not np.any(bad), f"{name}: {int(bad.sum())} entries off, worst {np.max(np.abs(x - ref)):.3e}"
+
+
+@dataclasses.dataclass
+class GpuResultEx:
+    status_f: int
+    loss: np.ndarray            # [1] (mean / sum) or [N] (none)
+    m: Optional[np.ndarray]
+    logs: Optional[np.ndarray]
+    status_b: Optional[int] = None
+    dH: Optional[np.ndarray] = None
+    dW: Optional[np.ndarray] = None
+    db: Optional[np.ndarray] = None
+    C: int = 0
+    idx: Optional[np.ndarray] = None
+
+
+def run_gpu_ex(wl: Workload, reduction: str, weights=None, num: float = 0.0, grad=None,
+               stats: bool = True, backward: bool = True, dev: str = "cuda:0"):
+    """compact -> lce_forward_ex -> lce_backward_ex through the C ABI.
+
+    weights: float[N] (host, numpy) or None; grad: None, a scalar (mean/sum)
+    or a float[N] array (none)."""
+    H = wl.H.to(dev)
+    W = wl.W.to(dev)
+    b = None if wl.b is None else wl.b.to(dev)
+    labels = wl.labels.to(dev)
+    mask = None if wl.mask is None else wl.mask.to(torch.uint8).to(dev)
+    N, D = H.shape
+    V = W.shape[0]
+    red = _lib.REDUCTIONS[reduction]
+    ws = torch.empty(_lib.lce_workspace_size(N, D, V, H.dtype), dtype=torch.uint8, device=dev)
+    idx = torch.full((max(N, 1),), -7, dtype=torch.int32, device=dev)
+    st_c, C = _lib.lce_compact_valid(labels, mask, V, wl.ignore_index, idx, ws)
+    assert st_c in (_lib.LCE_OK, _lib.LCE_OK_EMPTY), st_c
+    w = None if weights is None else torch.tensor(weights, dtype=torch.float32, device=dev)
+    loss = torch.full((N if red == _lib.LCE_REDUCTION_NONE else 1,), float("nan"), dtype=torch.float32,
+                      device=dev)
+    m = torch.full((N,), 12345.0, dtype=torch.float32, device=dev) if stats else None
+    logs = torch.full((N,), 12345.0, dtype=torch.float32, device=dev) if stats else None
+    st_f = _lib.lce_forward_ex(H, W, b, labels, idx, C, red, w, num, loss, m, logs, ws)
+    torch.cuda.synchronize()
+    r = GpuResultEx(st_f, to_np(loss), to_np(m), to_np(logs), C=C,
+                    idx=idx[:C].cpu().numpy().astype(np.int64))
+    if backward and stats and st_f in (_lib.LCE_OK, _lib.LCE_OK_EMPTY):
+        g = None
+        if grad is not None:
+            g = torch.tensor(np.atleast_1d(np.asarray(grad, dtype=np.float32)), device=dev)
+        dH = torch.full_like(H, 7.0)
+        dW = torch.full_like(W, 7.0)
+        db = None if b is None else torch.full_like(b, 7.0)
+        r.status_b = _lib.lce_backward_ex(H, W, b, labels, idx, C, red, w, num, m, logs, g, dH, dW, db, ws)
+        torch.cuda.synchronize()
+        r.dH, r.dW, r.db = to_np(dH), to_np(dW), to_np(db)
+    return r

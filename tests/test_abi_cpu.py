@@ -76,11 +76,26 @@ def test_host_argument_checks_return_before_any_hip_call(lib):
     assert lib.lce_forward(*args, 1, 2, 8, 8, 9, None, None, None, None, None, 0, None) == _lib.LCE_ERR_ARG
     # backward: dW missing
     assert lib.lce_backward(*args, 1, 2, 8, 8, 1, None, None, None, None, None, None, None, 0, None) == _lib.LCE_ERR_ARG
+    # reductions: unknown code, weights or a divisor outside SUM, negative / NaN / inf divisor
+    w = (ctypes.c_float * 4)()
+    out = (ctypes.c_float * 4)()
+    fe, be = lib.lce_forward_ex, lib.lce_backward_ex
+    assert fe(*args, 1, 2, 8, 8, 1, 7, None, 0.0, out, None, None, None, 0, None) == _lib.LCE_ERR_ARG
+    assert fe(*args, 1, 2, 8, 8, 1, _lib.LCE_REDUCTION_MEAN, w, 0.0, out, None, None, None, 0, None) == _lib.LCE_ERR_ARG
+    assert fe(*args, 1, 2, 8, 8, 1, _lib.LCE_REDUCTION_NONE, None, 3.0, out, None, None, None, 0, None) == _lib.LCE_ERR_ARG
+    for bad in (-1.0, float("nan"), float("inf")):
+        assert fe(*args, 1, 2, 8, 8, 1, _lib.LCE_REDUCTION_SUM, w, bad, out, None, None, None, 0, None) == _lib.LCE_ERR_ARG
+        assert be(*args, 1, 2, 8, 8, 1, _lib.LCE_REDUCTION_SUM, w, bad, None, None, None, None, None, None,
+                  None, 0, None) == _lib.LCE_ERR_ARG
+    assert be(*args, 1, 2, 8, 8, 1, 3, None, 0.0, None, None, None, None, None, None, None, 0, None) == _lib.LCE_ERR_ARG
+    # a valid reduction still rejects a missing loss output before any HIP call
+    assert fe(*args, 1, 2, 8, 8, 1, _lib.LCE_REDUCTION_SUM, None, 0.0, None, None, None, None, 0, None) == _lib.LCE_ERR_ARG
     # profiling switch validates its argument
     assert lib.lce_profile_start(0) == _lib.LCE_ERR_ARG
     assert lib.lce_profile_count() >= 0
 
 
 def test_python_binding_names_match_c_abi():
-    for n in ("lce_workspace_size", "lce_compact_valid", "lce_forward", "lce_backward"):
+    for n in ("lce_workspace_size", "lce_compact_valid", "lce_forward", "lce_backward", "lce_forward_ex",
+              "lce_backward_ex"):
         assert callable(getattr(_lib, n))

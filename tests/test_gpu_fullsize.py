@@ -11,6 +11,8 @@ Two kinds of checks, because the float64 oracle cannot afford all C rows:
     every output element against the oracle.
 """
 
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -88,3 +90,34 @@ def test_fullsize_sparse_supervision_elementwise(name):
     assert_grad_close("dW", r.dW, g.dW, t["grad"])
     if wl.b is not None:
         assert_grad_close("db", r.db, g.db, t["grad"])
+
+
+@pytest.mark.parametrize("name", ("packed", "stress"))
+def test_fullsize_weighted_sum_and_per_position(name):
+    """The reduction variants at full size: per-position losses (reduction
+    none) at sampled rows against the oracle; the weighted, divided sum equals
+    the fp64 sum of those per-position values; dH of the weighted sum at
+    sampled rows against the oracle with each row's factor lambda w_i / n."""
+    from lce_harness import run_gpu_ex
+    wl, Wd, bd = workload(name)
+    rng = np.random.default_rng(23)
+    w = rng.uniform(0.0, 2.0, wl.N).astype(np.float32)
+    num, lam = 0.5 * wl.N, 1.25
+    say(f"[fullsize] {name}: reduction none (forward only)")
+    rn = run_gpu_ex(wl, "none", backward=False)
+    say(f"[fullsize] {name}: weighted sum, forward + backward")
+    rs = run_gpu_ex(wl, "sum", w, num, lam)
+    assert rn.status_f == _lib.LCE_OK and rs.status_f == _lib.LCE_OK and rs.status_b == _lib.LCE_OK
+    idx = rs.idx
+    ref = math.fsum((w[idx].astype(np.float64) * rn.loss[idx]).tolist()) / num
+    assert abs(rs.loss[0] - ref) <= 1e-6 * abs(ref)
+    rows = np.unique(np.concatenate([np.sort(rng.choice(idx, size=6, replace=False)), idx[[0, -1]]]))
+    say(f"[fullsize] {name}: oracle on {rows.size} sampled rows")
+    Hs = wl.H[rows].double().numpy()
+    ys = wl.labels.numpy()[rows]
+    _, _, l = O.rows_forward(Hs, Wd, bd, ys)
+    t = tol(wl.dtype)
+    assert_stat_close("per-position loss", rn.loss[rows], l, t["stat"])
+    dh = np.concatenate([O.rows_grad_h(Hs[k:k + 1], Wd, bd, ys[k:k + 1], lam * float(w[rows[k]]) / num)
+                         for k in range(rows.size)])
+    assert_grad_close("dH rows", rs.dH[rows], dh, t["grad"])
