@@ -117,6 +117,11 @@ bool make_layout(int64_t N, int64_t D, int64_t V, lce_dtype_t dt, Layout& L) {
   L.nblk = cdiv(std::max<int64_t>(N, 1), kCmpBlock);
   L.Vpad = rup(V, 256);
   L.Vc = std::min<int64_t>(L.Vpad, kVcMax);
+  // The GEMM operands are addressed with 32-bit buffer offsets from a tile
+  // origin: keep one chunk of G (Npad x Vc) and of W (Vc x D) within 2 GB.
+  const int64_t vc_cap = std::min(((int64_t)1 << 31) / (L.Npad * esz), ((int64_t)1 << 31) / (D * esz)) / 256 * 256;
+  if (vc_cap < 256) return false;
+  L.Vc = std::min(L.Vc, vc_cap);
   size_t off = 0;
   auto take = [&](int64_t bytes) {
     const size_t o = off;
@@ -387,6 +392,11 @@ lce_status_t shape_supported(int64_t N, int64_t D, int64_t V, lce_dtype_t dt) {
   if (D % vec != 0) return LCE_ERR_UNSUPPORTED;
   if (N > (int64_t)1 << 30 || V > (int64_t)1 << 30 || D > (int64_t)1 << 20) return LCE_ERR_UNSUPPORTED;
   if (N * D > ((int64_t)1 << 40) || V * D > ((int64_t)1 << 40)) return LCE_ERR_UNSUPPORTED;
+  // 32-bit buffer offsets: the gathered rows (N x D) and one 256-row chunk of
+  // G must each stay within 2 GB.
+  const int64_t esz = dt == LCE_DTYPE_BF16 ? 2 : 4;
+  if (rup(std::max<int64_t>(N, 1), 256) * D * esz > ((int64_t)1 << 31)) return LCE_ERR_UNSUPPORTED;
+  if (rup(std::max<int64_t>(N, 1), 256) * 256 * esz > ((int64_t)1 << 31)) return LCE_ERR_UNSUPPORTED;
   return LCE_OK;
 }
 

@@ -40,7 +40,7 @@ template <> __device__ __forceinline__ uint16_t from_f32<uint16_t>(float x) {
 // ---------------------------------------------------------------- tile config
 template <typename T> struct Cfg;
 template <> struct Cfg<uint16_t> {
-  static constexpr int BM = 256, BN = 256, BK = 32;
+  static constexpr int BM = 256, BN = 256, BK = 32;  // BK: k granularity of the dH splits
   static constexpr int VEC = 8;     // elements per 16-byte vector
   static constexpr int KG = 4;      // k rows per transposed block (K-outer loader)
   static constexpr int ESZ = 2;

@@ -16,8 +16,18 @@
 
 #include "lce_device.h"
 #include "lce_pipe.h"
+#include "lce_pipe32.h"
 
 namespace lce {
+
+static_assert(Geo<uint16_t>::TM == pipe::TM && Geo<uint16_t>::TN == pipe::TN && Geo<uint16_t>::WGM == pipe::WGM &&
+                  Geo<uint16_t>::WGN == pipe::WGN && pipe::THREADS == kThreads && Cfg<uint16_t>::BM == pipe::BM &&
+                  Cfg<uint16_t>::BN == pipe::BN,
+              "the bf16 kernels and the BK=64 pipeline agree on the tile geometry");
+static_assert(Geo<uint16_t>::TM == pipe32::TM && Geo<uint16_t>::TN == pipe32::TN && Geo<uint16_t>::WGM == pipe32::WGM &&
+                  Geo<uint16_t>::WGN == pipe32::WGN && Cfg<uint16_t>::BK == pipe32::BK &&
+                  pipe::LDS_BYTES == pipe32::LDS_BYTES,
+              "the gradient kernel and the BK=32 pipeline agree on the tile geometry");
 
 // ============================================================== K0 compaction
 // a_i = 1[mask_i] 1[y_i != ignore] (section 01).  Three passes: per-block
@@ -322,7 +332,8 @@ __global__ __launch_bounds__(kThreads) void k_fwd(const T* __restrict__ W, const
     mrun[tn] = -INFINITY;
     srun[tn] = 0.f;
   }
-  const int nsteps = (D + C::BK - 1) / C::BK;
+  // Stages per tile: BK = 64 in the bf16 pipeline, Cfg<T>::BK in the fp32 loop.
+  const int nsteps = sizeof(T) == 2 ? (D + pipe::BK - 1) / pipe::BK : (D + C::BK - 1) / C::BK;
   float* red;
   if constexpr (sizeof(T) == 2) {
     f32x16_t acc[G::TM][G::TN];
@@ -655,7 +666,8 @@ __global__ __launch_bounds__(kThreads) void k_replay(
   const int vt0 = vg * tpw;
   const int ntiles = min(tpw, vtiles - vt0);
   const int n0 = rb * C::BN;
-  const int nsteps = (D + C::BK - 1) / C::BK;
+  // Stages per tile: BK = 64 in the bf16 pipeline, Cfg<T>::BK in the fp32 loop.
+  const int nsteps = sizeof(T) == 2 ? (D + pipe::BK - 1) / pipe::BK : (D + C::BK - 1) / C::BK;
   if constexpr (sizeof(T) == 2) {
     float* red = reinterpret_cast<float*>(smem_raw + pipe::RING_BYTES);
     f32x16_t acc[G::TM][G::TN];
@@ -715,11 +727,12 @@ __device__ __forceinline__ void grad_store(const f32x16_t (&acc)[Geo<T>::TM][Geo
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int r = m0 + wm * G::WTM + acc_row(tm, i, lane);
+        const float a = acc[tm][tn][i];
         if (dh) {
           float* p = slot + (int64_t)r * D + n;
-          *p = accumulate ? (*p + acc[tm][tn][i]) : acc[tm][tn][i];
+          *p = accumulate ? (*p + a) : a;
         } else if (r < vc) {
-          dW[(int64_t)(v0 + r) * D + n] = from_f32<T>(acc[tm][tn][i]);
+          dW[(int64_t)(v0 + r) * D + n] = from_f32<T>(a);
         }
       }
       // One 32x32 block at a time keeps the read-modify-write registers bounded.
@@ -794,9 +807,9 @@ __global__ __launch_bounds__(kThreads) void k_grad(
     };
     auto no_epi = [](int, f32x16_t (&)[G::TM][G::TN]) {};
     if (dh)
-      pipe::run<0, false>(1, nsteps, nsteps * C::BK, smem_raw, acc, origin, no_epi);
+      pipe32::run<0, false>(1, nsteps, nsteps * C::BK, smem_raw, acc, origin, no_epi);
     else
-      pipe::run<1, false>(1, nsteps, nsteps * C::BK, smem_raw, acc, origin, no_epi);
+      pipe32::run<1, false>(1, nsteps, nsteps * C::BK, smem_raw, acc, origin, no_epi);
     grad_store<T>(acc, dh, m0, n0, D, vc, v0, slot, accumulate, dW);
   } else {
     T* smem = reinterpret_cast<T*>(smem_raw);

@@ -1,23 +1,27 @@
 // bf16 MFMA GEMM pipeline for gfx950 built on direct-to-LDS buffer loads.
 //
-// One workgroup (8 wave64) computes a sequence of 256 x 256 output tiles.
-// Operand tiles travel global -> LDS with `buffer_load_dwordx4 ... lds`
-// (no staging registers), through a ring of NS = 4 LDS stages of BK = 32:
-// three stages are in flight while one is consumed, and the loads of the
-// next tile's first stages overlap the current tile's epilogue.  Each wave
-// waits only for its own loads (vmcnt) and one workgroup barrier per stage
-// publishes the stage and frees the slot that the next load overwrites.
+// One workgroup (8 wave64, two per SIMD) computes a sequence of 256 x 256
+// output tiles; each wave owns a 128 x 64 part (4 x 2 blocks of
+// v_mfma_f32_32x32x16_bf16).  Operand tiles travel
+// global -> LDS with `buffer_load_dwordx4 ... lds` (no staging registers) in
+// stages of BK = 64, through two LDS slots: while the MFMAs consume stage g
+// from registers, stage g+1 sits in LDS and stage g+2 is in flight.  A stage
+// is read into registers in four 16-wide k-substeps, double-buffered: the
+// fragments of substep j+1 are read while the MFMAs of substep j run.  One
+// workgroup barrier per stage publishes the next stage and frees the slot the
+// following load overwrites; the loads of the next tile's first stages
+// overlap the current tile's epilogue.
 //
-// LDS layouts (per operand and stage, 16 KB):
-//  * K-contiguous operand (element (r, k) at base[r*ld + k]): [r][k], 64-byte
-//    rows of four 16-byte chunks; chunk c of row r sits in slot
-//    c ^ ((r >> 2) & 3), so the 16 rows that one ds_read_b128 phase touches
-//    fall in 16 distinct bank groups.
-//  * K-outer operand (element (r, k) at base[k*ld + r]): [k][r], exactly as in
-//    global memory, 512-byte rows; 32-byte pairs permuted by XOR with
-//    2*(k & 3).  MFMA fragments come from ds_read_b64_tr_b16: within each
-//    16-lane group, lane i receives element i%4 of lane (4j + i/4)'s 8-byte
-//    chunk for j = 0..3, i.e. four consecutive k of one r.
+// LDS layouts (per operand and stage, 32 KB):
+//  * K-contiguous operand: [r][k], 128-byte rows of eight 16-byte chunks;
+//    chunk c of row r sits in slot c ^ ((r >> 1) & 7), so the 16 rows one
+//    ds_read_b128 phase touches fall in 16 distinct 16-byte bank groups.
+//    Each row is one full 128-byte line of the source per stage.
+//  * K-outer operand (element (r, k) at base[k*ld + r]): [k][r], 512-byte
+//    rows; 32-byte pairs permuted by XOR with 2*(k & 3).  MFMA fragments come
+//    from ds_read_b64_tr_b16: within each 16-lane group, lane i receives
+//    element i%4 of lane (4j + i/4)'s 8-byte chunk for j = 0..3, i.e. four
+//    consecutive k of one r.
 #pragma once
 
 #include "lce_device.h"
@@ -25,10 +29,11 @@
 namespace lce {
 namespace pipe {
 
-constexpr int BM = 256, BN = 256, BK = 32, NS = 4;
-constexpr int OPND_BYTES = 256 * BK * 2;          // one operand, one stage: 16 KB
+constexpr int BM = 256, BN = 256, BK = 64, NSLOT = 2;
+constexpr int NWAVES = 8, THREADS = 64 * NWAVES;
+constexpr int OPND_BYTES = 256 * BK * 2;          // one operand, one stage: 32 KB
 constexpr int STAGE_BYTES = 2 * OPND_BYTES;       // A then B
-constexpr int RING_BYTES = NS * STAGE_BYTES;      // 128 KB
+constexpr int RING_BYTES = NSLOT * STAGE_BYTES;   // 128 KB
 constexpr int SCRATCH_BYTES = 4096;               // epilogue scratch after the ring
 constexpr int BIAS_SLOTS = 4, BIAS_SLOT_BYTES = 1024;  // per-tile bias slices after the scratch
 constexpr int BIAS_OFFSET = RING_BYTES + SCRATCH_BYTES;
@@ -38,17 +43,17 @@ constexpr int LDS_BYTES = BIAS_OFFSET + BIAS_SLOTS * BIAS_SLOT_BYTES;
 __device__ __forceinline__ const uint16_t* bias_slice(const char* lds, int t) {
   return reinterpret_cast<const uint16_t*>(lds + BIAS_OFFSET + (t & (BIAS_SLOTS - 1)) * BIAS_SLOT_BYTES);
 }
-constexpr int WGM = 2, WGN = 4, WTM = 128, WTN = 64, TM = 4, TN = 2;
-constexpr int DMA_PER_OPND = OPND_BYTES / 1024 / 8;  // 1 KB DMA instructions per wave: 2
-constexpr int DMA_PER_STAGE = 2 * DMA_PER_OPND;      // 4 per wave per stage
+constexpr int WGM = 2, WGN = NWAVES / 2, WTM = BM / WGM, WTN = BN / WGN, TM = WTM / 32, TN = WTN / 32;
+constexpr int DMA_PER_OPND = OPND_BYTES / 1024 / NWAVES;  // 1 KB DMA instructions per wave: 8
+constexpr int DMA_PER_STAGE = 2 * DMA_PER_OPND;           // 16 per wave per stage
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
 // One operand of one output tile.
-//   K-contiguous: element (r, k) at base[r*ld + k*kstep] for k a multiple of
-//     32, plus k%32 (kstep = 1 for plain row-major; 256 for the blocked G
-//     layout, whose 256 x 32 blocks follow each other along k).
+//   K-contiguous: element (r, k) at base[r*ld + (k/32)*32*kstep + k%32]
+//     (kstep = 1: plain row-major; kstep = 256: the blocked G layout, whose
+//     256 x 32 blocks follow each other along k).
 //   K-outer: element (r, k) at base[k*ld + r], or, with bstride > 0 (blocked
 //     G read transposed), at base[(k/256)*bstride + (k%256)*32 + (r/32)*8192 + r%32].
 struct Opnd {
@@ -73,17 +78,6 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
-// Waits until at most `n` vector memory operations are outstanding, for the
-// n this pipeline produces: k*DMA_PER_STAGE (k = 0..2) plus optionally `extra`
-// younger operations (stores an epilogue issued after those loads).
-template <int EXTRA>
-__device__ __forceinline__ void wait_vmcnt_rt(int n) {
-  if (n >= 2 * DMA_PER_STAGE + EXTRA) wait_vmcnt<2 * DMA_PER_STAGE + EXTRA>();
-  else if (n >= DMA_PER_STAGE + EXTRA) wait_vmcnt<DMA_PER_STAGE + EXTRA>();
-  else if (n >= 2 * DMA_PER_STAGE) wait_vmcnt<2 * DMA_PER_STAGE>();
-  else if (n >= DMA_PER_STAGE) wait_vmcnt<DMA_PER_STAGE>();
-  else wait_vmcnt<0>();
-}
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xF | (7 << 4) | (0 << 8) | (3 << 14)); }
 // Workgroup barrier without a memory fence (a fence would drain every
 // in-flight LDS load); callers wait for what they need explicitly.
@@ -95,15 +89,19 @@ __device__ __forceinline__ void raw_barrier() {
 
 // ------------------------------------------------------------------ loads
 // Per-tile load plan of one operand: a buffer resource at the tile origin
-// and each lane's byte offsets for its DMA_PER_OPND instructions; a stage
-// only adds its k offset.  Rows past the operand's end fall past
-// num_records and load 0 in hardware.
+// and the byte offset of each of this wave's DMA_PER_OPND chunks at k = k0.
+// Chunk i of a lane sits at vb[i & 1] + ub + i * us: the lane-dependent part
+// only alternates with the parity of i, the rest is uniform, so a plan costs
+// 2 VGPRs per operand.  Offsets are whole byte offsets (never split into an
+// SGPR part), so rows past the operand's end fall past num_records and load
+// 0 in hardware.
 struct Plan {
   __amdgpu_buffer_rsrc_t rs;
-  uint32_t voff[DMA_PER_OPND];  // byte offsets at k = k0 of the tile
-  int kc8[DMA_PER_OPND];        // K-contiguous only: k offset of the lane's chunk
-  uint32_t kstride;             // bytes per unit of k (stages are 32-aligned)
-  uint32_t bstride_b;           // K-outer blocked: bytes between 256-row blocks (0 = plain)
+  uint32_t vb[2];      // lane part of the offsets of even / odd chunks
+  int kc8[2];          // K-contiguous only: k offset of the lane's even / odd chunk
+  uint32_t ub, us;     // uniform part: ub + i * us
+  uint32_t kstride;    // bytes per unit of k (stages are 64-aligned)
+  uint32_t bstride_b;  // K-outer blocked: bytes between 256-row blocks (0 = plain)
 };
 
 template <bool KC>
@@ -124,24 +122,35 @@ __device__ __forceinline__ void plan_opnd(Plan& p, const Opnd& o, int k0, int wa
     p.rs = make_rsrc(o.base + base, (o.elems - base) * 2);
     p.kstride = (uint32_t)(o.ld * 2);
   }
+  // Chunk q = (wave*DMA_PER_OPND + i)*64 + lane of the 32 KB stage tile.
+  if constexpr (KC) {
+    // row = q >> 3 = 8*(wave*DMA_PER_OPND + i) + (lane >> 3); slot = lane & 7;
+    // the chunk brings k chunk kc = slot ^ ((row >> 1) & 7), and
+    // (row >> 1) & 7 = (4*i + (lane >> 4)) & 7 depends on i only by parity.
 #pragma unroll
-  for (int i = 0; i < DMA_PER_OPND; ++i) {
-    const int q = (wave * DMA_PER_OPND + i) * 64 + lane;  // 16-byte chunk in the 16 KB tile
-    if constexpr (KC) {
-      const int row = q >> 2, slot = q & 3;
-      const int kc = slot ^ ((row >> 2) & 3);
-      p.voff[i] = (uint32_t)(((int64_t)row * o.ld + kc * 8) * 2);
-      p.kc8[i] = kc * 8;
-    } else {
-      const int kr = q >> 5, c = q & 31;
-      const int gp = (c >> 1) ^ (2 * (kr & 3));
+    for (int par = 0; par < 2; ++par) {
+      const int kc = (lane & 7) ^ ((4 * par + (lane >> 4)) & 7);
+      p.vb[par] = (uint32_t)(((int64_t)(lane >> 3) * o.ld + (int64_t)(kc >> 2) * 32 * o.kstep + (kc & 3) * 8) * 2);
+      p.kc8[par] = kc * 8;
+    }
+    p.us = (uint32_t)(8 * o.ld * 2);
+    p.ub = (uint32_t)(wave * DMA_PER_OPND) * p.us;
+  } else {
+    // kr = q >> 5 = 2*(wave*DMA_PER_OPND + i) + (lane >> 5); c = lane & 31;
+    // the 32-byte pair swizzle 2*(kr & 3) depends on i only by parity.
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      const int krl = lane >> 5, c = lane & 31;
+      const int gp = (c >> 1) ^ (2 * ((2 * par + krl) & 3));
       const int gv = 8 * (2 * gp + (c & 1));  // first r of the lane's 16-byte chunk
       if (o.bstride > 0)
-        p.voff[i] = (uint32_t)(((int64_t)kr * GB_COLS + (gv / GB_COLS) * GB_ELEMS + gv % GB_COLS) * 2);
+        p.vb[par] = (uint32_t)(((int64_t)krl * GB_COLS + (gv / GB_COLS) * GB_ELEMS + gv % GB_COLS) * 2);
       else
-        p.voff[i] = (uint32_t)(((int64_t)kr * o.ld + gv) * 2);
-      p.kc8[i] = 0;
+        p.vb[par] = (uint32_t)(((int64_t)krl * o.ld + gv) * 2);
+      p.kc8[par] = 0;
     }
+    p.us = o.bstride > 0 ? (uint32_t)(2 * GB_COLS * 2) : (uint32_t)(2 * o.ld * 2);
+    p.ub = (uint32_t)(wave * DMA_PER_OPND) * p.us;
   }
 }
 
@@ -150,7 +159,7 @@ __device__ __forceinline__ void plan_opnd(Plan& p, const Opnd& o, int k0, int wa
 // load 0 (only checked when the stage straddles it).
 template <bool KC>
 __device__ __forceinline__ void issue_plan(const Plan& p, int krel, int krel_end, char* lds_opnd, int wave) {
-  // Blocked K-outer: a stage stays inside one 256-row block (stages are 32
+  // Blocked K-outer: a stage stays inside one 256-row block (stages are 64
   // rows, blocks 256), so the stage offset is block base + row offset.
   uint32_t add = (uint32_t)krel * p.kstride;
   if constexpr (!KC)
@@ -158,8 +167,11 @@ __device__ __forceinline__ void issue_plan(const Plan& p, int krel, int krel_end
   const bool tail = KC && (krel + BK > krel_end);
 #pragma unroll
   for (int i = 0; i < DMA_PER_OPND; ++i) {
-    uint32_t off = p.voff[i] + add;
-    if (tail && krel + p.kc8[i] >= krel_end) off = kOobOffset;
+    // readfirstlane keeps the uniform sum in an SGPR computed here (not 8
+    // precomputed per-lane offsets held across the loop).
+    const uint32_t u = __builtin_amdgcn_readfirstlane(p.ub + (uint32_t)i * p.us + add);
+    uint32_t off = p.vb[i & 1] + u;
+    if (tail && krel + p.kc8[i & 1] >= krel_end) off = kOobOffset;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(p.rs, (lds_void*)(lds_opnd + (wave * DMA_PER_OPND + i) * 1024), 16,
                                              off, 0, 0, 0);
   }
@@ -167,13 +179,13 @@ __device__ __forceinline__ void issue_plan(const Plan& p, int krel, int krel_end
 
 // ------------------------------------------------------------------ fragments
 // 8 bf16 along k for MFMA lane `lane`: row/col r_base + (lane & 31),
-// k = 16*kk + 8*(lane >> 5) + 0..7.
+// k = 16*kk + 8*(lane >> 5) + 0..7 (kk = 0..3 within the stage).
 template <bool KC>
 __device__ __forceinline__ u32x4 load_frag(const char* lds_opnd, int r_base, int kk, int lane) {
   if constexpr (KC) {
     const int R = r_base + (lane & 31);
     const int kc = 2 * kk + (lane >> 5);
-    return *reinterpret_cast<const u32x4*>(lds_opnd + R * 64 + ((kc ^ ((R >> 2) & 3)) << 4));
+    return *reinterpret_cast<const u32x4*>(lds_opnd + R * 128 + ((kc ^ ((R >> 1) & 7)) << 4));
   } else {
     const int a = lane & 15;
     const int n = r_base + 16 * ((lane >> 4) & 1) + 4 * (a & 3);
@@ -194,15 +206,16 @@ __device__ __forceinline__ u32x4 load_frag_a(const char* sa, int r_base, int kk,
   else if constexpr (A_MODE == 1) return load_frag<false>(sa, r_base, kk, lane);
   else return a_kc ? load_frag<true>(sa, r_base, kk, lane) : load_frag<false>(sa, r_base, kk, lane);
 }
-// Operand fragments of one k-substep (16 k) of one stage.
+// Operand fragments of one k-substep (16 k) of one stage.  (Used for
+// K-contiguous operands; a K-outer fragment takes two transposing reads.)
 template <int A_MODE, bool B_KC>
 struct Frags {
   u32x4 a[TM], b[TN];
   __device__ __forceinline__ void load(const char* st, int kk, int wm, int wn, int lane, bool a_kc) {
 #pragma unroll
-    for (int tn = 0; tn < TN; ++tn) b[tn] = load_frag<B_KC>(st + OPND_BYTES, wn * WTN + tn * 32, kk, lane);
-#pragma unroll
     for (int tm = 0; tm < TM; ++tm) a[tm] = load_frag_a<A_MODE>(st, wm * WTM + tm * 32, kk, lane, a_kc);
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) b[tn] = load_frag<B_KC>(st + OPND_BYTES, wn * WTN + tn * 32, kk, lane);
   }
   __device__ __forceinline__ void mma(f32x16_t (&acc)[TM][TN]) const {
 #pragma unroll
@@ -213,8 +226,21 @@ struct Frags {
                                                               __builtin_bit_cast(bf16x8_t, b[tn]),
                                                               acc[tm][tn], 0, 0, 0);
   }
-  static constexpr int kReads = (TM * (A_MODE == 0 ? 1 : 2)) + TN * (B_KC ? 1 : 2);
+  // LDS read instructions per substep (a transposed fragment takes two).
+  static constexpr int kReads = TM * (A_MODE == 0 ? 1 : 2) + TN * (B_KC ? 1 : 2);
 };
+
+// Interleaves a substep's R LDS reads with its M MFMAs in the schedule.
+template <int R, int M>
+__device__ __forceinline__ void interleave() {
+  if constexpr (R > 0) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, M / R, 0);
+    interleave<R - 1, M - M / R>();
+  } else if constexpr (M > 0) {
+    __builtin_amdgcn_sched_group_barrier(0x008, M, 0);
+  }
+}
 
 __device__ __forceinline__ void zero(f32x16_t (&acc)[TM][TN]) {
 #pragma unroll
@@ -236,24 +262,25 @@ __device__ __forceinline__ void zero(f32x16_t (&acc)[TM][TN]) {
 // after the call, holds the last tile's sums (single-tile callers store it
 // themselves after run() instead of inside the pipelined loop).
 // EPI_STORES: vector memory operations every wave's epilogue certainly
-// issues after its last load wait (an undercount is safe: the wait after an
-// epilogue then also drains some of them).  Vector memory operations retire
-// in issue order on this target, so younger stores need not be waited for.
+// issues (an undercount is safe: the first stage wait after an epilogue then
+// also drains some of them).  Vector memory operations retire in issue order
+// on this target, so those younger stores need not be waited for.
 // With `bias` (A K-contiguous, A.r0 = the tile's first vocabulary row),
 // wave 0 also loads each tile's 256 bias values into bias_slice(lds, t),
 // right before that tile's first stage: the stage wait that publishes the
-// stage publishes the slice too.  A slot is reloaded 4 tiles later, after the
-// barrier that follows the last epilogue that read it ((4-1)*nsteps >= 3).
+// stage publishes the slice too.  A slot is reloaded 4 tiles later, after
+// the barriers that follow the last epilogue that read it.
 template <int A_MODE, bool B_KC, int EPI_STORES = 0, typename Origin, typename Epi>
 __device__ __forceinline__ void run(int ntiles, int nsteps, int kend, char* lds, f32x16_t (&acc)[TM][TN],
                                     Origin origin, Epi epi, bool a_kc = true,
                                     const uint16_t* bias = nullptr, int V = 0) {
-  static_assert(BK == 32, "Frags covers the two 16-wide k-substeps of a stage");
+  static_assert(BK == 64, "four 16-wide k-substeps per stage");
+  using F = Frags<A_MODE, B_KC>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave % WGM, wn = wave / WGM;
   const int total = ntiles * nsteps;
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform: keeps LDS targets scalar
-  // Issue state (the next global step to load).
+  // Issue state (the next global stage to load).
   int it = 0, is = 0;
   Plan pA, pB;
   int bias_m0 = 0;
@@ -270,7 +297,7 @@ __device__ __forceinline__ void run(int ntiles, int nsteps, int kend, char* lds,
   };
   plan_tile(0);
   auto issue_next = [&](int g) {
-    char* st = lds + (g % NS) * STAGE_BYTES;
+    char* st = lds + (g & 1) * STAGE_BYTES;
     if (bias != nullptr && is == 0 && wave_s == 0) {
       const __amdgpu_buffer_rsrc_t rb = make_rsrc(bias + bias_m0, (int64_t)(V - bias_m0) * 2);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(lds + BIAS_OFFSET + (it & (BIAS_SLOTS - 1)) * BIAS_SLOT_BYTES),
@@ -286,39 +313,54 @@ __device__ __forceinline__ void run(int ntiles, int nsteps, int kend, char* lds,
       if (++it < ntiles) plan_tile(it);
     }
   };
-#pragma unroll
-  for (int g = 0; g < NS - 1; ++g)
-    if (g < total) issue_next(g);
+  issue_next(0);
+  if (total > 1) issue_next(1);
+  // Stage 0 must have landed (stage 1 may stay in flight).
+  if (total > 1) wait_vmcnt<DMA_PER_STAGE>();
+  else wait_vmcnt<0>();
+  raw_barrier();
+  F x, y;
+  x.load(lds, 0, wm, wn, lane, a_kc);
 
-  // One barrier per stage: it publishes stage g (each wave waited for its
-  // own loads) and frees the slot of stage g-1 for the load of stage g+3.
-  // Per stage: all LDS fragment reads, then the next loads, then the MFMAs.
-  int t = 0, s = 0;
-  for (int g = 0; g < total; ++g) {
-    // Stage g must have landed; later stages already issued may stay in
-    // flight, and so may the stores of an epilogue that ran just before.
-    const int later = DMA_PER_STAGE * min(NS - 2, total - 1 - g);
-    if (EPI_STORES > 0 && s == 0 && g > 0 && later > 0)
-      wait_vmcnt_rt<EPI_STORES>(later + EPI_STORES);
-    else
-      wait_vmcnt_rt<0>(later);
-    raw_barrier();
-    if (s == 0) zero(acc);
-    const char* st = lds + (g % NS) * STAGE_BYTES;
-    Frags<A_MODE, B_KC> f0, f1;
-    f0.load(st, 0, wm, wn, lane, a_kc);
-    f1.load(st, 1, wm, wn, lane, a_kc);
-    if (g + NS - 1 < total) issue_next(g + NS - 1);
-    f0.mma(acc);
-    f1.mma(acc);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * Frags<A_MODE, B_KC>::kReads, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 2 * TM * TN, 0);
-    if (++s == nsteps) {
-      epi(t, acc);
-      s = 0;
-      ++t;
+  // Per stage g (slot g & 1): substeps 0..2 each wait for their fragments,
+  // read the next substep's and run their MFMAs.  Before substep 3's MFMAs
+  // each wave has finished its reads of slot g (lgkm wait) and has its loads
+  // of stage g+1 landed (vm wait); the barrier makes both true for the whole
+  // workgroup, so slot g then takes stage g+2 and the first fragments of
+  // stage g+1 are read.
+  for (int t = 0; t < ntiles; ++t) {
+    zero(acc);
+    for (int s = 0; s < nsteps; ++s) {
+      const int g = t * nsteps + s;
+      const char* st = lds + (g & 1) * STAGE_BYTES;
+      wait_lgkm0();
+      y.load(st, 1, wm, wn, lane, a_kc);
+      x.mma(acc);
+      interleave<F::kReads, TM * TN>();
+      wait_lgkm0();
+      x.load(st, 2, wm, wn, lane, a_kc);
+      y.mma(acc);
+      interleave<F::kReads, TM * TN>();
+      wait_lgkm0();
+      y.load(st, 3, wm, wn, lane, a_kc);
+      x.mma(acc);
+      interleave<F::kReads, TM * TN>();
+      wait_lgkm0();
+      if (g + 1 < total) {
+        // Stage g+1 must have landed; the stores of an epilogue that ran
+        // after its loads were issued may stay in flight.
+        if (EPI_STORES > 0 && s == 0 && t > 0) wait_vmcnt<EPI_STORES>();
+        else wait_vmcnt<0>();
+      }
+      raw_barrier();
+      if (g + 2 < total) issue_next(g + 2);
+      if (g + 1 < total) x.load(lds + ((g + 1) & 1) * STAGE_BYTES, 0, wm, wn, lane, a_kc);
+      y.mma(acc);
+      interleave<F::kReads, TM * TN>();
     }
+    epi(t, acc);
   }
+  wait_lgkm0();
   raw_barrier();
 }
 
