@@ -39,8 +39,10 @@ def parse():
     p.add_argument("--steps", type=int, default=12)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="packed")
-    p.add_argument("--mode", choices=("train", "forward"), default="train",
-                   help="train: compaction + forward + backward; forward: compaction + forward-only loss")
+    p.add_argument("--mode", choices=("train", "forward", "shard"), default="train",
+                   help="train: compaction + forward + backward; forward: compaction + forward-only loss; "
+                        "shard: train with the vocabulary split into --shards shards run one after another")
+    p.add_argument("--shards", type=int, default=8, help="vocabulary shards for --mode shard")
     p.add_argument("--reduction", choices=("mean", "sum", "none"), default="mean",
                    help="mean: plain entries; sum (per-position weights, divisor N) / none: the _ex entries")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -187,9 +189,34 @@ def main():
         gen = torch.Generator().manual_seed(78)
         grad = torch.randn(N, generator=gen).to(dev)
     plain = args.reduction == "mean"
-    train = args.mode == "train"
+    train = args.mode in ("train", "shard")
+    if args.mode == "shard":
+        P = args.shards
+        bounds = [V * p // P for p in range(P + 1)]
+        parts = torch.empty(P * 3 * N, dtype=torch.float32, device=dev)  # [P][3*C] for C <= N
+        dH_parts = [torch.empty_like(H) for _ in range(P)]
+        g1 = grad if args.reduction == "none" else grad.reshape(1)
 
-    def step():
+        def step():
+            st, C = _lib.lce_compact_valid(labels, mask, V, wl.ignore_index, idx, ws, stream)
+            assert st == _lib.LCE_OK, _lib.status_string(st)
+            for p in range(P):
+                v0, v1 = bounds[p], bounds[p + 1]
+                st = _lib.lce_forward_shard(H, W[v0:v1], None if b is None else b[v0:v1], labels, idx, C, v0,
+                                            parts[p * 3 * C:(p + 1) * 3 * C], ws, stream)
+                assert st == _lib.LCE_OK, _lib.status_string(st)
+            pc = parts[: P * 3 * C].view(P, 3 * C)
+            st = _lib.lce_merge_shards(pc, bounds, labels, idx, C, red, weights, num, loss, m, logs, ws, stream)
+            assert st == _lib.LCE_OK, _lib.status_string(st)
+            for p in range(P):
+                v0, v1 = bounds[p], bounds[p + 1]
+                st = _lib.lce_backward_shard(H, W[v0:v1], None if b is None else b[v0:v1], labels, idx, C, v0, red,
+                                             weights, num, m, logs, g1, dH_parts[p], dW[v0:v1],
+                                             None if db is None else db[v0:v1], ws, stream)
+                assert st == _lib.LCE_OK, _lib.status_string(st)
+            return C
+
+    def step_single():
         st, C = _lib.lce_compact_valid(labels, mask, V, wl.ignore_index, idx, ws, stream)
         assert st == _lib.LCE_OK, _lib.status_string(st)
         if plain and train:
@@ -207,6 +234,9 @@ def main():
                                       ws, stream)
         assert st == _lib.LCE_OK, _lib.status_string(st)
         return C
+
+    if args.mode != "shard":
+        step = step_single
 
     for i in range(args.warmup):
         C = step()
@@ -271,6 +301,8 @@ def main():
 
     out = {
         "metric": METRIC if train else METRIC_FWD,
+        "note": (f"{args.shards} vocabulary shards run one after another; the dH sum over shards (an "
+                 "all-reduce across devices) is not part of the step") if args.mode == "shard" else None,
         "value": C * args.steps / (total_ms * 1e-3),
         "unit": "supervised tokens/s",
         "n_gpus": 1,
@@ -284,7 +316,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "N": N, "D": D, "V": V, "C": C,
                    "bias": b is not None, "mask": mask is not None, "mode": args.mode,
-                   "reduction": args.reduction},
+                   "reduction": args.reduction, "shards": args.shards if args.mode == "shard" else 1},
         "tflops": tflops,
         "pct_peak": 100.0 * tflops / peak,
         "positions_per_s": N * args.steps / (total_ms * 1e-3),

@@ -164,6 +164,58 @@ lce_status_t lce_backward_ex(const void* H, const void* W, const void* b, const 
                              const float* grad_loss, void* dH, void* dW, void* db, void* ws,
                              size_t ws_bytes, void* stream);
 
+/* ---- Vocabulary sharding on one device --------------------------------------
+ * The exchange that splitting W over P devices needs (glenzli.com page,
+ * section 02: the running (m, s) of disjoint vocabulary ranges merge exactly;
+ * AIInfraGuide chapter 2, the online-softmax merge): each shard computes
+ * per-row partials over its own vocabulary range, one merge combines them in
+ * shard order, and each shard's backward uses the merged statistics.  Here
+ * the shards run one after another on one device; across devices the parts
+ * would travel by an all-gather and the dH partials would be summed by an
+ * all-reduce. */
+
+/* Forward partials of one vocabulary shard: rows [v_begin, v_begin + V_shard)
+ * of the full W.
+ *   W_shard [V_shard, D], b_shard [V_shard] or NULL: device, type dt.
+ *   labels, valid_idx, C, N, D: as for lce_forward (labels are full-vocabulary
+ *            ids; labels outside the shard simply match no column here).
+ *   part     float[3*C] device, written: part[c] = m_c, part[C + c] = s_c
+ *            (exp-sum relative to m_c) over the shard's entries, and
+ *            part[2C + c] = the score of the row's target when its label lies
+ *            in the shard, else 0.
+ *   ws       workspace of lce_workspace_size(N, D, V_shard, dt) bytes.
+ * C == 0: returns LCE_OK_EMPTY and writes nothing. */
+lce_status_t lce_forward_shard(const void* H, const void* W_shard, const void* b_shard, const int64_t* labels,
+                               const int32_t* valid_idx, int64_t C, int64_t N, int64_t D, int64_t V_shard,
+                               int64_t v_begin, lce_dtype_t dt, float* part, void* ws, size_t ws_bytes,
+                               void* stream);
+
+/* Merge of P shard partials (shard order) into the loss and the statistics.
+ *   parts        float[P][3*C] device: the `part` outputs of the P shards.
+ *   P            1..64 shards.
+ *   shard_begin  host int64[P+1]: shard p covers labels [shard_begin[p],
+ *                shard_begin[p+1]); shard_begin[0] = 0, strictly increasing,
+ *                shard_begin[P] = V.
+ *   reduction, loss_weights, num_label_tokens, loss, m, logs: as for
+ *                lce_forward_ex (m, logs may be NULL).
+ *   ws           device scratch of at least 4*C bytes.
+ * C == 0: loss 0 (zeros for NONE), m = logs = -inf, LCE_OK_EMPTY. */
+lce_status_t lce_merge_shards(const float* parts, int32_t P, const int64_t* shard_begin, const int64_t* labels,
+                              const int32_t* valid_idx, int64_t C, int64_t N, lce_reduction_t reduction,
+                              const float* loss_weights, double num_label_tokens, float* loss, float* m,
+                              float* logs, void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of one vocabulary shard from the merged m / logs: dW_shard
+ * [V_shard, D] and db_shard [V_shard] (or NULL) of the shard's rows, and
+ * dH_part [N, D], this shard's share of dH (the sum over shards is dH).
+ * Other arguments as for lce_backward_ex; ws as for lce_forward_shard. */
+lce_status_t lce_backward_shard(const void* H, const void* W_shard, const void* b_shard, const int64_t* labels,
+                                const int32_t* valid_idx, int64_t C, int64_t N, int64_t D, int64_t V_shard,
+                                int64_t v_begin, lce_dtype_t dt, lce_reduction_t reduction,
+                                const float* loss_weights, double num_label_tokens, const float* m,
+                                const float* logs, const float* grad_loss, void* dH_part, void* dW_shard,
+                                void* db_shard, void* ws, size_t ws_bytes, void* stream);
+
 /* Static string for a status code. */
 const char* lce_status_string(lce_status_t status);
 

@@ -38,6 +38,9 @@ EXPORTS = (
     "lce_backward",
     "lce_forward_ex",
     "lce_backward_ex",
+    "lce_forward_shard",
+    "lce_merge_shards",
+    "lce_backward_shard",
     "lce_status_string",
     "lce_profile_start",
     "lce_profile_stop",
@@ -80,6 +83,14 @@ def load() -> ctypes.CDLL:
     lib.lce_backward_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
                                     ctypes.c_int, vp, dbl, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.lce_backward_ex.restype = ctypes.c_int
+    lib.lce_forward_shard.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int, vp, vp, sz, vp]
+    lib.lce_forward_shard.restype = ctypes.c_int
+    lib.lce_merge_shards.argtypes = [vp, i32, ctypes.POINTER(i64), vp, vp, i64, i64, ctypes.c_int, vp, dbl, vp, vp,
+                                     vp, vp, sz, vp]
+    lib.lce_merge_shards.restype = ctypes.c_int
+    lib.lce_backward_shard.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int, vp,
+                                       dbl, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.lce_backward_shard.restype = ctypes.c_int
     lib.lce_status_string.argtypes = [ctypes.c_int]
     lib.lce_status_string.restype = ctypes.c_char_p
     lib.lce_profile_start.argtypes = [i32]
@@ -167,6 +178,36 @@ def lce_backward_ex(H, W, b, labels, valid_idx, C: int, reduction: int, loss_wei
                                   dtype_code(H.dtype), int(reduction), _ptr(loss_weights),
                                   float(num_label_tokens), _ptr(m), _ptr(logs), _ptr(grad_loss), _ptr(dH),
                                   _ptr(dW), _ptr(db), _ptr(ws), ws.numel(), _stream_ptr(stream))
+
+
+def lce_forward_shard(H, W_shard, b_shard, labels, valid_idx, C: int, v_begin: int, part, ws, stream=None) -> int:
+    N, D = H.shape
+    Vs = W_shard.shape[0]
+    return load().lce_forward_shard(_ptr(H), _ptr(W_shard), _ptr(b_shard), _ptr(labels), _ptr(valid_idx), C, N, D,
+                                    Vs, v_begin, dtype_code(H.dtype), _ptr(part), _ptr(ws), ws.numel(),
+                                    _stream_ptr(stream))
+
+
+def lce_merge_shards(parts, shard_begin, labels, valid_idx, C: int, reduction: int, loss_weights,
+                     num_label_tokens: float, loss, m, logs, ws, stream=None) -> int:
+    """parts: float32[P, 3*C] (device); shard_begin: P+1 ints (host)."""
+    P = len(shard_begin) - 1
+    arr = (ctypes.c_int64 * (P + 1))(*[int(x) for x in shard_begin])
+    N = labels.numel()
+    return load().lce_merge_shards(_ptr(parts), P, arr, _ptr(labels), _ptr(valid_idx), C, N, int(reduction),
+                                   _ptr(loss_weights), float(num_label_tokens), _ptr(loss), _ptr(m), _ptr(logs),
+                                   _ptr(ws), ws.numel(), _stream_ptr(stream))
+
+
+def lce_backward_shard(H, W_shard, b_shard, labels, valid_idx, C: int, v_begin: int, reduction: int, loss_weights,
+                       num_label_tokens: float, m, logs, grad_loss, dH_part, dW_shard, db_shard, ws,
+                       stream=None) -> int:
+    N, D = H.shape
+    Vs = W_shard.shape[0]
+    return load().lce_backward_shard(_ptr(H), _ptr(W_shard), _ptr(b_shard), _ptr(labels), _ptr(valid_idx), C, N, D,
+                                     Vs, v_begin, dtype_code(H.dtype), int(reduction), _ptr(loss_weights),
+                                     float(num_label_tokens), _ptr(m), _ptr(logs), _ptr(grad_loss), _ptr(dH_part),
+                                     _ptr(dW_shard), _ptr(db_shard), _ptr(ws), ws.numel(), _stream_ptr(stream))
 
 
 def profile_start(max_launches: int = 65536) -> None:

@@ -264,9 +264,9 @@ lce_status_t fill_f32(float* p, int64_t n, float v, hipStream_t s) {
 // ------------------------------------------------------------------ forward
 template <typename T>
 lce_status_t forward_impl(const T* H, const T* W, const T* b, const int64_t* labels,
-                          const int32_t* idx, int64_t C, int64_t N, int64_t D, int64_t V,
+                          const int32_t* idx, int64_t C, int64_t N, int64_t D, int64_t V, int64_t label_off,
                           const Reduce& red, float* loss, float* m, float* logs, float* row_loss,
-                          char* ws, const Layout& L, hipStream_t s) {
+                          float* shard_part, char* ws, const Layout& L, hipStream_t s) {
   using Cf = Cfg<T>;
   const int Cpad = (int)rup(C, 256);
   T* Hc = reinterpret_cast<T*>(ws + L.hc);
@@ -279,7 +279,7 @@ lce_status_t forward_impl(const T* H, const T* W, const T* b, const int64_t* lab
   {
     const int64_t vec = (int64_t)Cpad * (D / (16 / (int64_t)sizeof(T)));
     const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(cdiv(vec, 256), 8192));
-    LCE_LAUNCH("k_gather", (k_gather<T>), grid, 256, 0, s, H, labels, idx, (int)C, Cpad, (int)D, Hc,
+    LCE_LAUNCH("k_gather", (k_gather<T>), grid, 256, 0, s, H, labels, idx, (int)C, Cpad, (int)D, label_off, Hc,
                yc, (const float*)nullptr, (const float*)nullptr, (float*)nullptr, (float*)nullptr);
   }
   const int n_rb = Cpad / Cf::BN;
@@ -290,6 +290,11 @@ lce_status_t forward_impl(const T* H, const T* W, const T* b, const int64_t* lab
   set_lds_attr<T>((const void*)k_fwd<T>, gemm_lds_bytes<T>());
   LCE_LAUNCH("k_fwd", (k_fwd<T>), per_xcd * 8, kThreads, gemm_lds_bytes<T>(), s, W, b, Hc, yc, Cpad,
              (int)D, (int)V, n_rb, n_split, n_vt, n_work, per_xcd, pm, ps, tgt);
+  if (shard_part) {  // vocabulary shard: the row partials only
+    LCE_LAUNCH("k_shard_partial", k_shard_partial, cdiv(C, 256), 256, 0, s, pm, ps, tgt, n_split, Cpad, (int)C, yc,
+               (int)V, shard_part, shard_part + C, shard_part + 2 * C);
+    return LCE_OK;
+  }
   LCE_TRY(fill_f32(m, N, -INFINITY, s));
   LCE_TRY(fill_f32(logs, N, -INFINITY, s));
   LCE_TRY(fill_f32(row_loss, N, 0.f, s));
@@ -304,7 +309,7 @@ lce_status_t forward_impl(const T* H, const T* W, const T* b, const int64_t* lab
 // ------------------------------------------------------------------ backward
 template <typename T>
 lce_status_t backward_impl(const T* H, const T* W, const T* b, const int64_t* labels,
-                           const int32_t* idx, int64_t C, int64_t N, int64_t D, int64_t V,
+                           const int32_t* idx, int64_t C, int64_t N, int64_t D, int64_t V, int64_t label_off,
                            const Reduce& red, const float* m, const float* logs, const float* grad_loss,
                            T* dH, T* dW, T* db, char* ws, const Layout& L, hipStream_t s) {
   using Cf = Cfg<T>;
@@ -325,7 +330,7 @@ lce_status_t backward_impl(const T* H, const T* W, const T* b, const int64_t* la
   {
     const int64_t vec = (int64_t)Cpad * (D / (16 / (int64_t)sizeof(T)));
     const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(cdiv(vec, 256), 8192));
-    LCE_LAUNCH("k_gather", (k_gather<T>), grid, 256, 0, s, H, labels, idx, (int)C, Cpad, (int)D, Hc,
+    LCE_LAUNCH("k_gather", (k_gather<T>), grid, 256, 0, s, H, labels, idx, (int)C, Cpad, (int)D, label_off, Hc,
                yc, m, logs, mc, lsc);
   }
   {
@@ -415,7 +420,8 @@ lce_status_t make_reduce(int kind, const float* weights, double num, Reduce& r) 
 lce_status_t forward_entry(const void* H, const void* W, const void* b, const int64_t* labels,
                            const int32_t* valid_idx, int64_t C, int64_t N, int64_t D, int64_t V,
                            lce_dtype_t dt, const Reduce& red, float* loss, float* m, float* logs,
-                           float* row_loss, void* ws, size_t ws_bytes, void* stream) {
+                           float* row_loss, void* ws, size_t ws_bytes, void* stream, int64_t label_off = 0,
+                           float* shard_part = nullptr) {
   try {
     if (!dims_ok(N, D, V, dt) || C < 0 || C > N) return LCE_ERR_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -435,9 +441,10 @@ lce_status_t forward_entry(const void* H, const void* W, const void* b, const in
     char* w = static_cast<char*>(ws);
     if (dt == LCE_DTYPE_BF16)
       return forward_impl<uint16_t>((const uint16_t*)H, (const uint16_t*)W, (const uint16_t*)b, labels,
-                                    valid_idx, C, N, D, V, red, loss, m, logs, row_loss, w, L, s);
+                                    valid_idx, C, N, D, V, label_off, red, loss, m, logs, row_loss, shard_part, w,
+                                    L, s);
     return forward_impl<float>((const float*)H, (const float*)W, (const float*)b, labels, valid_idx, C,
-                               N, D, V, red, loss, m, logs, row_loss, w, L, s);
+                               N, D, V, label_off, red, loss, m, logs, row_loss, shard_part, w, L, s);
   } catch (...) {
     return LCE_ERR_HIP;
   }
@@ -448,7 +455,7 @@ lce_status_t backward_entry(const void* H, const void* W, const void* b, const i
                             const int32_t* valid_idx, int64_t C, int64_t N, int64_t D, int64_t V,
                             lce_dtype_t dt, const Reduce& red, const float* m, const float* logs,
                             const float* grad_loss, void* dH, void* dW, void* db, void* ws,
-                            size_t ws_bytes, void* stream) {
+                            size_t ws_bytes, void* stream, int64_t label_off = 0) {
   try {
     if (!dims_ok(N, D, V, dt) || C < 0 || C > N) return LCE_ERR_ARG;
     if (!dW || (N > 0 && !dH)) return LCE_ERR_ARG;
@@ -470,10 +477,10 @@ lce_status_t backward_entry(const void* H, const void* W, const void* b, const i
     char* w = static_cast<char*>(ws);
     if (dt == LCE_DTYPE_BF16)
       return backward_impl<uint16_t>((const uint16_t*)H, (const uint16_t*)W, (const uint16_t*)b, labels,
-                                     valid_idx, C, N, D, V, red, m, logs, grad_loss, (uint16_t*)dH,
+                                     valid_idx, C, N, D, V, label_off, red, m, logs, grad_loss, (uint16_t*)dH,
                                      (uint16_t*)dW, (uint16_t*)db, w, L, s);
     return backward_impl<float>((const float*)H, (const float*)W, (const float*)b, labels, valid_idx, C,
-                                N, D, V, red, m, logs, grad_loss, (float*)dH, (float*)dW, (float*)db, w,
+                                N, D, V, label_off, red, m, logs, grad_loss, (float*)dH, (float*)dW, (float*)db, w,
                                 L, s);
   } catch (...) {
     return LCE_ERR_HIP;
@@ -584,6 +591,70 @@ lce_status_t lce_backward_ex(const void* H, const void* W, const void* b, const 
   LCE_TRY(make_reduce(reduction, loss_weights, num_label_tokens, red));
   return backward_entry(H, W, b, labels, valid_idx, C, N, D, V, dt, red, m, logs, grad_loss, dH, dW, db, ws,
                         ws_bytes, stream);
+}
+
+lce_status_t lce_forward_shard(const void* H, const void* W_shard, const void* b_shard, const int64_t* labels,
+                               const int32_t* valid_idx, int64_t C, int64_t N, int64_t D, int64_t V_shard,
+                               int64_t v_begin, lce_dtype_t dt, float* part, void* ws, size_t ws_bytes,
+                               void* stream) {
+  if (v_begin < 0 || C < 0 || C > N) return LCE_ERR_ARG;
+  if (C == 0) return LCE_OK_EMPTY;  // no rows: no partials
+  if (!part) return LCE_ERR_ARG;
+  return forward_entry(H, W_shard, b_shard, labels, valid_idx, C, N, D, V_shard, dt, Reduce{}, nullptr, nullptr,
+                       nullptr, nullptr, ws, ws_bytes, stream, v_begin, part);
+}
+
+lce_status_t lce_merge_shards(const float* parts, int32_t P, const int64_t* shard_begin, const int64_t* labels,
+                              const int32_t* valid_idx, int64_t C, int64_t N, lce_reduction_t reduction,
+                              const float* loss_weights, double num_label_tokens, float* loss, float* m,
+                              float* logs, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    Reduce red;
+    LCE_TRY(make_reduce(reduction, loss_weights, num_label_tokens, red));
+    if (N < 0 || C < 0 || C > N || !loss || P < 1 || P > kMaxShards || !shard_begin) return LCE_ERR_ARG;
+    ShardBounds bounds{};
+    if (shard_begin[0] != 0) return LCE_ERR_ARG;
+    for (int p = 0; p <= P; ++p) {
+      if (p > 0 && shard_begin[p] <= shard_begin[p - 1]) return LCE_ERR_ARG;
+      bounds.b[p] = shard_begin[p];
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    float* row_loss = red.kind == kReduceNone ? loss : nullptr;
+    if (C == 0) {
+      if (red.kind != kReduceNone) LCE_LAUNCH("k_store_scalar", k_store_scalar, 1, 1, 0, s, loss, 0.f);
+      LCE_TRY(fill_f32(m, N, -INFINITY, s));
+      LCE_TRY(fill_f32(logs, N, -INFINITY, s));
+      LCE_TRY(fill_f32(row_loss, N, 0.f, s));
+      return LCE_OK_EMPTY;
+    }
+    if (!parts || !labels || !valid_idx || !ws) return LCE_ERR_ARG;
+    if (ws_bytes < (size_t)C * sizeof(float)) return LCE_ERR_WORKSPACE;
+    float* lrow = static_cast<float*>(ws);
+    LCE_TRY(fill_f32(m, N, -INFINITY, s));
+    LCE_TRY(fill_f32(logs, N, -INFINITY, s));
+    LCE_TRY(fill_f32(row_loss, N, 0.f, s));
+    LCE_LAUNCH("k_merge_shards", k_merge_shards, cdiv(C, 256), 256, 0, s, parts, parts + C, parts + 2 * C, (int)P,
+               3 * C, bounds, labels, valid_idx, (int)C, m, logs, row_loss, lrow);
+    if (red.kind != kReduceNone)
+      LCE_LAUNCH("k_loss_sum", k_loss_sum, 1, 1024, 0, s, lrow, (int)C, (int)red.kind, red.weights, valid_idx,
+                 red.div, loss);
+    return LCE_OK;
+  } catch (...) {
+    return LCE_ERR_HIP;
+  }
+}
+
+lce_status_t lce_backward_shard(const void* H, const void* W_shard, const void* b_shard, const int64_t* labels,
+                                const int32_t* valid_idx, int64_t C, int64_t N, int64_t D, int64_t V_shard,
+                                int64_t v_begin, lce_dtype_t dt, lce_reduction_t reduction,
+                                const float* loss_weights, double num_label_tokens, const float* m,
+                                const float* logs, const float* grad_loss, void* dH_part, void* dW_shard,
+                                void* db_shard, void* ws, size_t ws_bytes, void* stream) {
+  Reduce red;
+  LCE_TRY(make_reduce(reduction, loss_weights, num_label_tokens, red));
+  if (v_begin < 0) return LCE_ERR_ARG;
+  return backward_entry(H, W_shard, b_shard, labels, valid_idx, C, N, D, V_shard, dt, red, m, logs, grad_loss,
+                        dH_part, dW_shard, db_shard, ws, ws_bytes, stream, v_begin);
 }
 
 lce_status_t lce_profile_start(int32_t max_launches) {

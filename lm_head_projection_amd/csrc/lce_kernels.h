@@ -148,7 +148,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void k_gather(const T* __restrict__ H,
                                                 const int64_t* __restrict__ labels,
                                                 const int32_t* __restrict__ idx, int C, int Cpad,
-                                                int D, T* __restrict__ Hc, int* __restrict__ yc,
+                                                int D, int64_t label_off, T* __restrict__ Hc, int* __restrict__ yc,
                                                 const float* __restrict__ m,
                                                 const float* __restrict__ logs, float* mc,
                                                 float* lsc) {
@@ -166,7 +166,13 @@ __global__ __launch_bounds__(256) void k_gather(const T* __restrict__ H,
     }
     *reinterpret_cast<u32x4*>(Hc + (int64_t)c * D + kv * VEC) = v;
     if (kv == 0) {
-      yc[c] = c < C ? (int)labels[src] : -1;
+      // Labels relative to the first vocabulary row of W (a vocabulary shard
+      // starts at label_off); a label outside [0, V) of that W matches no column.
+      yc[c] = -1;
+      if (c < C) {
+        const int64_t yl = labels[src] - label_off;
+        yc[c] = (yl >= 0 && yl < INT32_MAX) ? (int)yl : -1;
+      }
       if (mc) {
         mc[c] = c < C ? m[src] : INFINITY;
         lsc[c] = c < C ? logs[src] : 0.f;
@@ -412,6 +418,57 @@ __global__ __launch_bounds__(256) void k_merge(const float* __restrict__ pm, con
   const float ls = logf(s);
   const float l = (m - tgt[c]) + ls;
   const int n = idx[c];
+  if (m_out) m_out[n] = m;
+  if (logs_out) logs_out[n] = ls;
+  if (row_loss) row_loss[n] = l;
+  lrow[c] = l;
+}
+
+// Vocabulary shard (the partials one tensor-parallel rank would send): per
+// supervised row, the split partials of this shard merged in split order
+// into (m, s), and the target score when the row's label falls in the shard
+// (0 otherwise; the cross-shard merge reads it only from the owning shard).
+__global__ __launch_bounds__(256) void k_shard_partial(const float* __restrict__ pm, const float* __restrict__ ps,
+                                                       const float* __restrict__ tgt, int n_split, int Cpad, int C,
+                                                       const int* __restrict__ yc, int Vs, float* __restrict__ out_m,
+                                                       float* __restrict__ out_s, float* __restrict__ out_t) {
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= C) return;
+  float m = -INFINITY, s = 0.f;
+  for (int k = 0; k < n_split; ++k) lse_merge(m, s, pm[(int64_t)k * Cpad + c], ps[(int64_t)k * Cpad + c]);
+  out_m[c] = m;
+  out_s[c] = s;
+  out_t[c] = ((unsigned)yc[c] < (unsigned)Vs) ? tgt[c] : 0.f;
+}
+
+// Shard boundaries (vocabulary starts of P shards, then V): a kernel argument.
+constexpr int kMaxShards = 64;
+struct ShardBounds {
+  int64_t b[kMaxShards + 1];
+};
+
+// Cross-shard merge (the exchange step of vocabulary sharding): per supervised
+// row, the P shard partials merged in shard order (section 02 recurrence),
+// the target score taken from the shard holding y_i, l_i = (m - z_y) + log s;
+// m, log s and l scattered to the row's position as in k_merge.
+__global__ __launch_bounds__(256) void k_merge_shards(const float* __restrict__ part_m,
+                                                      const float* __restrict__ part_s,
+                                                      const float* __restrict__ part_t, int P, int64_t ld,
+                                                      ShardBounds bounds, const int64_t* __restrict__ labels,
+                                                      const int32_t* __restrict__ idx, int C,
+                                                      float* __restrict__ m_out, float* __restrict__ logs_out,
+                                                      float* __restrict__ row_loss, float* __restrict__ lrow) {
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= C) return;
+  float m = -INFINITY, s = 0.f;
+  for (int p = 0; p < P; ++p) lse_merge(m, s, part_m[(int64_t)p * ld + c], part_s[(int64_t)p * ld + c]);
+  const int n = idx[c];
+  const int64_t y = labels[n];
+  int owner = 0;
+  for (int p = 0; p < P; ++p)
+    if (y >= bounds.b[p] && y < bounds.b[p + 1]) owner = p;
+  const float ls = logf(s);
+  const float l = (m - part_t[(int64_t)owner * ld + c]) + ls;
   if (m_out) m_out[n] = m;
   if (logs_out) logs_out[n] = ls;
   if (row_loss) row_loss[n] = l;

@@ -90,6 +90,20 @@ def test_host_argument_checks_return_before_any_hip_call(lib):
     assert be(*args, 1, 2, 8, 8, 1, 3, None, 0.0, None, None, None, None, None, None, None, 0, None) == _lib.LCE_ERR_ARG
     # a valid reduction still rejects a missing loss output before any HIP call
     assert fe(*args, 1, 2, 8, 8, 1, _lib.LCE_REDUCTION_SUM, None, 0.0, None, None, None, None, 0, None) == _lib.LCE_ERR_ARG
+    # vocabulary shards: P out of range, bounds not starting at 0 or not increasing, negative v_begin
+    i64 = ctypes.c_int64
+    loss1 = (ctypes.c_float * 1)()
+    ws4 = (ctypes.c_float * 64)()
+    good = (i64 * 3)(0, 5, 9)
+    for P, bnd in ((0, good), (65, good), (2, (i64 * 3)(1, 5, 9)), (2, (i64 * 3)(0, 5, 5)), (2, (i64 * 3)(0, 7, 3))):
+        assert lib.lce_merge_shards(out, P, bnd, None, None, 3, 4, _lib.LCE_REDUCTION_MEAN, None, 0.0, loss1,
+                                    None, None, ws4, 256, None) == _lib.LCE_ERR_ARG
+    assert lib.lce_merge_shards(out, 2, good, None, None, 3, 4, 9, None, 0.0, loss1, None, None, ws4, 256,
+                                None) == _lib.LCE_ERR_ARG
+    assert lib.lce_forward_shard(*args, 1, 2, 8, 8, -1, 1, out, None, 0, None) == _lib.LCE_ERR_ARG
+    assert lib.lce_forward_shard(*args, 1, 2, 8, 8, 0, 1, None, None, 0, None) == _lib.LCE_ERR_ARG
+    assert lib.lce_backward_shard(*args, 1, 2, 8, 8, -1, 1, 0, None, 0.0, None, None, None, None, None, None,
+                                  None, 0, None) == _lib.LCE_ERR_ARG
     # profiling switch validates its argument
     assert lib.lce_profile_start(0) == _lib.LCE_ERR_ARG
     assert lib.lce_profile_count() >= 0
@@ -97,5 +111,5 @@ def test_host_argument_checks_return_before_any_hip_call(lib):
 
 def test_python_binding_names_match_c_abi():
     for n in ("lce_workspace_size", "lce_compact_valid", "lce_forward", "lce_backward", "lce_forward_ex",
-              "lce_backward_ex"):
+              "lce_backward_ex", "lce_forward_shard", "lce_merge_shards", "lce_backward_shard"):
         assert callable(getattr(_lib, n))

@@ -121,3 +121,26 @@ def test_fullsize_weighted_sum_and_per_position(name):
     dh = np.concatenate([O.rows_grad_h(Hs[k:k + 1], Wd, bd, ys[k:k + 1], lam * float(w[rows[k]]) / num)
                          for k in range(rows.size)])
     assert_grad_close("dH rows", rs.dH[rows], dh, t["grad"])
+
+
+def test_fullsize_packed_eight_vocabulary_shards():
+    """The packed workload split into 8 vocabulary shards of ~31040 rows (one
+    tensor-parallel rank's share of an 8-way split) matches the unsharded run:
+    loss, m, log s within fp32 rounding of a different merge order; dW rows
+    and the summed dH partials within the gradient tolerance."""
+    from test_gpu_shards import run_sharded
+    wl, Wd, bd = workload("packed")
+    V = wl.V
+    bounds = [V * p // 8 for p in range(9)]
+    say("[fullsize] packed: unsharded")
+    r0 = run_gpu(wl)
+    say("[fullsize] packed: 8 shards")
+    r1 = run_sharded(wl, bounds)
+    assert abs(r1["loss"][0] - r0.loss) <= 1e-5 * abs(r0.loss)
+    a = np.zeros(wl.N, dtype=bool)
+    a[r0.idx] = True
+    assert_stat_close("m", r1["m"][a], r0.m[a], 1e-5)
+    assert_stat_close("logs", r1["logs"][a], r0.logs[a], 1e-5)
+    t = tol(wl.dtype)
+    assert_grad_close("dW", r1["dW"], r0.dW, t["grad"])
+    assert_grad_close("dH", r1["dH"], r0.dH, t["grad"])
