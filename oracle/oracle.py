@@ -248,6 +248,52 @@ def dense_backward(H, W, b, labels, m, logs, lam: float = 1.0, mask=None,
     return BackwardResult(dH, dW, db)
 
 
+def filtered_backward(H, W, b, labels, m, logs, eps: float, lam: float = 1.0, mask=None,
+                      ignore_index: int = IGNORE_INDEX, row_block: int = 256,
+                      col_block: int = 32) -> BackwardResult:
+    """Gradient filtering of small-probability blocks (the CCE threshold
+    filter that glenzli.com section 07 describes as an approximation of the
+    full gradient).  Reading of the pages: the supervised rows, in ascending
+    position order, are cut into blocks of `row_block` rows and the
+    vocabulary into blocks of `col_block` entries; a block whose
+    probabilities p_ij are all below `eps` and which holds no row's target
+    column contributes nothing to dH and dW.  db keeps every contribution.
+    eps = 0 keeps every block (the exact gradient).
+    """
+    H = _f64(H)
+    W = _f64(W)
+    b = _f64(b)
+    N, D = H.shape
+    V = W.shape[0]
+    a, idx, C = supervised_rows(labels, mask, ignore_index)
+    check_labels(labels, idx, V)
+    y = np.asarray(labels, dtype=np.int64)
+    dH = np.zeros((N, D))
+    dW = np.zeros((V, D))
+    db = np.zeros(V)
+    if C == 0:
+        return BackwardResult(dH, dW, db)
+    scale = lam / C
+    for lo in range(0, C, row_block):
+        rows = idx[lo:lo + row_block]
+        Z = logits(H[rows], W, b)
+        P = np.exp((Z - m[rows][:, None]) - logs[rows][:, None])
+        G = P.copy()
+        G[np.arange(rows.size), y[rows]] -= 1.0
+        G *= scale
+        db += G.sum(axis=0)
+        keep = np.zeros_like(G)
+        for v0 in range(0, V, col_block):
+            v1 = min(V, v0 + col_block)
+            has_target = np.any((y[rows] >= v0) & (y[rows] < v1))
+            if has_target or np.max(P[:, v0:v1]) >= eps:
+                keep[:, v0:v1] = 1.0
+        Gf = G * keep
+        dH[rows] = Gf @ W
+        dW += Gf.T @ H[rows]
+    return BackwardResult(dH, dW, db)
+
+
 def dense_forward_backward(H, W, b, labels, mask=None, lam: float = 1.0,
                            ignore_index: int = IGNORE_INDEX,
                            row_block: Optional[int] = None):

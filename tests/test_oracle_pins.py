@@ -504,3 +504,60 @@ def test_reductions_empty_supervision():
     assert O.reduce_rows(f.row_loss, f.idx, f.C, "sum", np.ones(4), 9.0) == 0.0
     assert np.all(O.reduce_rows(f.row_loss, f.idx, f.C, "none") == 0.0)
     assert np.all(O.row_factors(4, f.idx, f.C, "none", np.ones(4)) == 0.0)
+
+
+# ---------------------------------------------------------------- gradient filtering (glenzli.com section 07)
+def _filter_case(seed=40, N=40, D=6, V=200, peak=6.0):
+    """Rows whose softmax is peaked on a few entries, so that some blocks
+    fall far below a threshold and others far above."""
+    rng = np.random.default_rng(seed)
+    H = rng.standard_normal((N, D))
+    W = 0.3 * rng.standard_normal((V, D))
+    W[:40] += peak * rng.standard_normal((40, D)) / np.sqrt(D)
+    b = 0.1 * rng.standard_normal(V)
+    y = rng.integers(0, 40, N)
+    y[[3, 17]] = -100
+    return H, W, b, y
+
+
+def test_filter_eps_zero_is_the_exact_gradient():
+    H, W, b, y = _filter_case()
+    f, g = O.dense_forward_backward(H, W, b, y)
+    gf = O.filtered_backward(H, W, b, y, f.m, f.logs, 0.0, row_block=16)
+    np.testing.assert_allclose(gf.dH, g.dH, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(gf.dW, g.dW, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(gf.db, g.db, rtol=1e-12, atol=1e-15)
+
+
+def test_filter_error_within_bound_and_db_exact():
+    """|dropped contribution| <= (lam/C) * eps * sum_j |W_j| per dH entry (every
+    dropped p is below eps), and likewise for dW with |H_i|; db is exact."""
+    H, W, b, y = _filter_case()
+    lam, eps = 1.7, 1e-3
+    f, g = O.dense_forward_backward(H, W, b, y, None, lam)
+    gf = O.filtered_backward(H, W, b, y, f.m, f.logs, eps, lam, row_block=16)
+    C = f.C
+    bound_h = lam / C * eps * np.sum(np.abs(W), axis=0)[None, :]
+    assert np.all(np.abs(gf.dH - g.dH) <= bound_h + 1e-15)
+    bound_w = lam / C * eps * np.sum(np.abs(H[f.idx]), axis=0)[None, :]
+    assert np.all(np.abs(gf.dW - g.dW) <= bound_w + 1e-15)
+    np.testing.assert_allclose(gf.db, g.db, rtol=1e-12, atol=1e-15)
+    # something was dropped, and something kept
+    assert np.max(np.abs(gf.dW - g.dW)) > 0
+    assert np.max(np.abs(gf.dW)) > 0
+
+
+def test_filter_huge_eps_keeps_only_target_blocks():
+    """eps > 1: only blocks that hold a target column survive; with one row
+    block (all rows) and blocks of 32 columns, dW is exactly zero outside the
+    32-wide blocks that contain some supervised label."""
+    H, W, b, y = _filter_case()
+    f = O.dense_forward(H, W, b, y)
+    gf = O.filtered_backward(H, W, b, y, f.m, f.logs, 2.0, row_block=1000)
+    live = np.zeros(W.shape[0], dtype=bool)
+    for lab in y[f.idx]:
+        live[(lab // 32) * 32:(lab // 32) * 32 + 32] = True
+    assert np.all(gf.dW[~live] == 0.0)
+    # and those blocks keep their exact contribution (every row's whole block)
+    f2, g2 = O.dense_forward_backward(H, W, b, y)
+    np.testing.assert_allclose(gf.dW[live], g2.dW[live], rtol=1e-12, atol=1e-15)
