@@ -43,6 +43,8 @@ def parse():
                    help="train: compaction + forward + backward; forward: compaction + forward-only loss; "
                         "shard: train with the vocabulary split into --shards shards run one after another")
     p.add_argument("--shards", type=int, default=8, help="vocabulary shards for --mode shard")
+    p.add_argument("--filter-eps", type=float, default=None,
+                   help="train with the gradient filter at this threshold (lce_backward_filtered)")
     p.add_argument("--reduction", choices=("mean", "sum", "none"), default="mean",
                    help="mean: plain entries; sum (per-position weights, divisor N) / none: the _ex entries")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -227,7 +229,10 @@ def main():
         assert st == _lib.LCE_OK, _lib.status_string(st)
         if not train:
             return C
-        if plain:
+        if args.filter_eps is not None:
+            st = _lib.lce_backward_filtered(H, W, b, labels, idx, C, red, weights, num, m, logs, grad,
+                                            args.filter_eps, dH, dW, db, ws, stream)
+        elif plain:
             st = _lib.lce_backward(H, W, b, labels, idx, C, m, logs, grad, dH, dW, db, ws, stream)
         else:
             st = _lib.lce_backward_ex(H, W, b, labels, idx, C, red, weights, num, m, logs, grad, dH, dW, db,
@@ -316,7 +321,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "N": N, "D": D, "V": V, "C": C,
                    "bias": b is not None, "mask": mask is not None, "mode": args.mode,
-                   "reduction": args.reduction, "shards": args.shards if args.mode == "shard" else 1},
+                   "reduction": args.reduction, "shards": args.shards if args.mode == "shard" else 1,
+                   "filter_eps": args.filter_eps},
         "tflops": tflops,
         "pct_peak": 100.0 * tflops / peak,
         "positions_per_s": N * args.steps / (total_ms * 1e-3),

@@ -38,6 +38,7 @@ EXPORTS = (
     "lce_backward",
     "lce_forward_ex",
     "lce_backward_ex",
+    "lce_backward_filtered",
     "lce_forward_shard",
     "lce_merge_shards",
     "lce_backward_shard",
@@ -83,6 +84,9 @@ def load() -> ctypes.CDLL:
     lib.lce_backward_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
                                     ctypes.c_int, vp, dbl, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.lce_backward_ex.restype = ctypes.c_int
+    lib.lce_backward_filtered.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int, vp,
+                                          dbl, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, sz, vp]
+    lib.lce_backward_filtered.restype = ctypes.c_int
     lib.lce_forward_shard.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int, vp, vp, sz, vp]
     lib.lce_forward_shard.restype = ctypes.c_int
     lib.lce_merge_shards.argtypes = [vp, i32, ctypes.POINTER(i64), vp, vp, i64, i64, ctypes.c_int, vp, dbl, vp, vp,
@@ -178,6 +182,16 @@ def lce_backward_ex(H, W, b, labels, valid_idx, C: int, reduction: int, loss_wei
                                   dtype_code(H.dtype), int(reduction), _ptr(loss_weights),
                                   float(num_label_tokens), _ptr(m), _ptr(logs), _ptr(grad_loss), _ptr(dH),
                                   _ptr(dW), _ptr(db), _ptr(ws), ws.numel(), _stream_ptr(stream))
+
+
+def lce_backward_filtered(H, W, b, labels, valid_idx, C: int, reduction: int, loss_weights, num_label_tokens: float,
+                          m, logs, grad_loss, eps: float, dH, dW, db, ws, stream=None) -> int:
+    N, D = H.shape
+    V = W.shape[0]
+    return load().lce_backward_filtered(_ptr(H), _ptr(W), _ptr(b), _ptr(labels), _ptr(valid_idx), C, N, D, V,
+                                        dtype_code(H.dtype), int(reduction), _ptr(loss_weights),
+                                        float(num_label_tokens), _ptr(m), _ptr(logs), _ptr(grad_loss), float(eps),
+                                        _ptr(dH), _ptr(dW), _ptr(db), _ptr(ws), ws.numel(), _stream_ptr(stream))
 
 
 def lce_forward_shard(H, W_shard, b_shard, labels, valid_idx, C: int, v_begin: int, part, ws, stream=None) -> int:

@@ -103,7 +103,7 @@ struct Layout {
   // forward
   size_t pm, ps, tgt, lrow;
   // backward
-  size_t mc, lsc, rsc, inv, G, slots, dbp;
+  size_t mc, lsc, rsc, inv, G, slots, dbp, flags;
   size_t total;
   int64_t Npad, Vpad, Vc, nblk;
 };
@@ -150,6 +150,7 @@ bool make_layout(int64_t N, int64_t D, int64_t V, lce_dtype_t dt, Layout& L) {
   L.G = take(L.Npad * L.Vc * esz);
   L.slots = take((int64_t)kDhSlotRows * L.Npad * D * 4);
   L.dbp = take((L.Npad / bn) * L.Vpad * 4);
+  L.flags = take((L.Npad / 256) * (L.Vc / 32));  // gradient filter: live G blocks of one chunk
   L.total = std::max(off, fwd_end);
   return true;
 }
@@ -311,7 +312,8 @@ template <typename T>
 lce_status_t backward_impl(const T* H, const T* W, const T* b, const int64_t* labels,
                            const int32_t* idx, int64_t C, int64_t N, int64_t D, int64_t V, int64_t label_off,
                            const Reduce& red, const float* m, const float* logs, const float* grad_loss,
-                           T* dH, T* dW, T* db, char* ws, const Layout& L, hipStream_t s) {
+                           T* dH, T* dW, T* db, char* ws, const Layout& L, hipStream_t s,
+                           float filter_eps = -1.f) {
   using Cf = Cfg<T>;
   const int Cpad = (int)rup(C, 256);
   T* Hc = reinterpret_cast<T*>(ws + L.hc);
@@ -343,8 +345,12 @@ lce_status_t backward_impl(const T* H, const T* W, const T* b, const int64_t* la
   const int n_rb = Cpad / Cf::BN;
   const int n_nt = (int)cdiv(D, Cf::BN);
   const int n_dh_mt = Cpad / Cf::BM;
-  set_lds_attr<T>((const void*)k_replay<T>, gemm_lds_bytes<T>());
-  set_lds_attr<T>((const void*)k_grad<T>, gemm_lds_bytes<T>());
+  const bool filter = filter_eps >= 0.f;
+  uint8_t* flags = filter ? reinterpret_cast<uint8_t*>(ws + L.flags) : nullptr;
+  const int64_t fstride = L.Vc / 32;
+  set_lds_attr<T>((const void*)k_replay<T, false>, gemm_lds_bytes<T>());
+  set_lds_attr<T>((const void*)k_replay<T, true>, gemm_lds_bytes<T>());
+  set_lds_attr<T>((const void*)k_grad<T>, grad_lds_bytes<T>());
 
   int S = 0;  // dH k-splits, fixed by the first (widest) chunk
   for (int64_t v0 = 0, chunk = 0; v0 < V; v0 += L.Vc, ++chunk) {
@@ -356,9 +362,16 @@ lce_status_t backward_impl(const T* H, const T* W, const T* b, const int64_t* la
       const int tpw = choose_tiles_per_wg(n_rb, vtiles);
       const int n_work = n_rb * (int)cdiv(vtiles, tpw);
       const int per_xcd = (int)cdiv(n_work, 8);
-      LCE_LAUNCH("k_replay", (k_replay<T>), per_xcd * 8, kThreads, gemm_lds_bytes<T>(), s, W, b, Hc,
-                 yc, mc, lsc, rsc, Cpad, (int)D, (int)V, (int)v0, vtiles, tpw, n_rb, n_work, per_xcd, Gc, ldg,
-                 db ? dbp : (float*)nullptr, lddb);
+      if (filter) {
+        LCE_TRY(zero_bytes(flags, (int64_t)n_rb * fstride, s));
+        LCE_LAUNCH("k_replay", (k_replay<T, true>), per_xcd * 8, kThreads, gemm_lds_bytes<T>(), s, W, b, Hc,
+                   yc, mc, lsc, rsc, Cpad, (int)D, (int)V, (int)v0, vtiles, tpw, n_rb, n_work, per_xcd, Gc, ldg,
+                   db ? dbp : (float*)nullptr, lddb, flags, fstride, filter_eps);
+      } else {
+        LCE_LAUNCH("k_replay", (k_replay<T, false>), per_xcd * 8, kThreads, gemm_lds_bytes<T>(), s, W, b, Hc,
+                   yc, mc, lsc, rsc, Cpad, (int)D, (int)V, (int)v0, vtiles, tpw, n_rb, n_work, per_xcd, Gc, ldg,
+                   db ? dbp : (float*)nullptr, lddb, (uint8_t*)nullptr, (int64_t)0, 0.f);
+      }
     }
     // K5: dH split so that one dH tile's K matches one dW tile's K (= Cpad).
     if (chunk == 0)
@@ -369,9 +382,9 @@ lce_status_t backward_impl(const T* H, const T* W, const T* b, const int64_t* la
     const int n_dw = vtiles * n_nt;
     const int per_xcd = (int)(cdiv(n_dh, 8) + cdiv(n_dw, 8));
     const int dh_first = ks_len >= Cpad ? 1 : 0;
-    LCE_LAUNCH("k_grad", (k_grad<T>), per_xcd * 8, kThreads, gemm_lds_bytes<T>(), s, Gc, ldg, kpad, Hc,
+    LCE_LAUNCH("k_grad", (k_grad<T>), per_xcd * 8, kThreads, grad_lds_bytes<T>(), s, Gc, ldg, kpad, Hc,
                W, Cpad, (int)D, (int)v0, vc, (int)(V - v0), n_nt, n_dh_mt, (int)ks_len, n_dh, vtiles,
-               dh_first, slots, slot_stride, chunk == 0 ? 0 : 1, dW);
+               dh_first, slots, slot_stride, chunk == 0 ? 0 : 1, dW, (const uint8_t*)flags, fstride);
   }
   {
     const int64_t vec = N * (D / 4);
@@ -455,7 +468,7 @@ lce_status_t backward_entry(const void* H, const void* W, const void* b, const i
                             const int32_t* valid_idx, int64_t C, int64_t N, int64_t D, int64_t V,
                             lce_dtype_t dt, const Reduce& red, const float* m, const float* logs,
                             const float* grad_loss, void* dH, void* dW, void* db, void* ws,
-                            size_t ws_bytes, void* stream, int64_t label_off = 0) {
+                            size_t ws_bytes, void* stream, int64_t label_off = 0, float filter_eps = -1.f) {
   try {
     if (!dims_ok(N, D, V, dt) || C < 0 || C > N) return LCE_ERR_ARG;
     if (!dW || (N > 0 && !dH)) return LCE_ERR_ARG;
@@ -478,7 +491,8 @@ lce_status_t backward_entry(const void* H, const void* W, const void* b, const i
     if (dt == LCE_DTYPE_BF16)
       return backward_impl<uint16_t>((const uint16_t*)H, (const uint16_t*)W, (const uint16_t*)b, labels,
                                      valid_idx, C, N, D, V, label_off, red, m, logs, grad_loss, (uint16_t*)dH,
-                                     (uint16_t*)dW, (uint16_t*)db, w, L, s);
+                                     (uint16_t*)dW, (uint16_t*)db, w, L, s, filter_eps);
+    if (filter_eps >= 0.f) return LCE_ERR_UNSUPPORTED;  // the filter runs on the bf16 path only
     return backward_impl<float>((const float*)H, (const float*)W, (const float*)b, labels, valid_idx, C,
                                 N, D, V, label_off, red, m, logs, grad_loss, (float*)dH, (float*)dW, (float*)db, w,
                                 L, s);
@@ -655,6 +669,20 @@ lce_status_t lce_backward_shard(const void* H, const void* W_shard, const void* 
   if (v_begin < 0) return LCE_ERR_ARG;
   return backward_entry(H, W_shard, b_shard, labels, valid_idx, C, N, D, V_shard, dt, red, m, logs, grad_loss,
                         dH_part, dW_shard, db_shard, ws, ws_bytes, stream, v_begin);
+}
+
+lce_status_t lce_backward_filtered(const void* H, const void* W, const void* b, const int64_t* labels,
+                                   const int32_t* valid_idx, int64_t C, int64_t N, int64_t D, int64_t V,
+                                   lce_dtype_t dt, lce_reduction_t reduction, const float* loss_weights,
+                                   double num_label_tokens, const float* m, const float* logs,
+                                   const float* grad_loss, float eps, void* dH, void* dW, void* db, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  Reduce red;
+  LCE_TRY(make_reduce(reduction, loss_weights, num_label_tokens, red));
+  if (!(eps >= 0.f) || std::isinf(eps)) return LCE_ERR_ARG;
+  if (dt != LCE_DTYPE_BF16) return dims_ok(N, D, V, dt) ? LCE_ERR_UNSUPPORTED : LCE_ERR_ARG;
+  return backward_entry(H, W, b, labels, valid_idx, C, N, D, V, dt, red, m, logs, grad_loss, dH, dW, db, ws,
+                        ws_bytes, stream, 0, eps);
 }
 
 lce_status_t lce_profile_start(int32_t max_launches) {

@@ -548,7 +548,10 @@ __global__ void k_store_scalar(float* __restrict__ p, float v) { p[0] = v; }
 // by its factor r_c (k_row_scale), write G = r_c (p - onehot) into the chunk
 // buffer, and, with a bias, the per-row-block column sums of G (db partials)
 // in a fixed order.
-template <typename T>
+// FILTER: also mark, per block of 256 rows x 32 vocabulary entries of G, whether
+// the block is live for the gradient GEMMs (see k_grad): some entry with
+// |r| p >= eps |r| (r != 0), or the block holds a row's target column.
+template <typename T, bool FILTER = false>
 __device__ __forceinline__ void replay_epilogue(f32x16_t (&acc)[Geo<T>::TM][Geo<T>::TN],
                                                 const T* __restrict__ bias, int m0, int n0, int V, int v0,
                                                 const int* __restrict__ yc, const float* __restrict__ mc,
@@ -556,7 +559,9 @@ __device__ __forceinline__ void replay_epilogue(f32x16_t (&acc)[Geo<T>::TM][Geo<
                                                 T* __restrict__ Gc,
                                                 int64_t ldg, float* __restrict__ dbp, int64_t lddb,
                                                 int rb, float* red, bool raw_sync,
-                                                const uint16_t* bias_slice = nullptr) {
+                                                const uint16_t* bias_slice = nullptr,
+                                                uint8_t* __restrict__ flags = nullptr, int64_t fstride = 0,
+                                                float eps = 0.f) {
   using C = Cfg<T>;
   using G = Geo<T>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -620,6 +625,32 @@ __device__ __forceinline__ void replay_epilogue(f32x16_t (&acc)[Geo<T>::TM][Geo<
         if (vbase + acc_row(tm, i, lane) >= V)
 #pragma unroll
           for (int tn = 0; tn < G::TN; ++tn) acc[tm][tn][i] = 0.f;
+  }
+  if constexpr (FILTER) {
+    // Block (row block n0/256, chunk column block (vbase - v0)/32 + tm):
+    // every wave holding part of it votes; any live entry marks it (the
+    // marks of different waves all write 1).  Ragged columns are 0 here.
+    float thr[G::TN];  // eps |r|, or +inf for rows with r = 0 (never live)
+    int dd[G::TN];
+#pragma unroll
+    for (int tn = 0; tn < G::TN; ++tn) {
+      const int r = n0 + wn * G::WTN + tn * 32 + (lane & 31);
+      const float ar = fabsf(rsc[r]);
+      thr[tn] = ar > 0.f ? eps * ar : INFINITY;
+      dd[tn] = yc[r] - vbase;
+    }
+    uint8_t* frow = flags + (int64_t)(n0 / C::BN) * fstride + (vbase - v0) / 32;
+#pragma unroll
+    for (int tm = 0; tm < G::TM; ++tm) {
+      bool live = false;
+#pragma unroll
+      for (int tn = 0; tn < G::TN; ++tn) {
+        live = live || (unsigned)(dd[tn] - tm * 32) < 32u;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) live = live || fabsf(acc[tm][tn][i]) >= thr[tn];
+      }
+      if (__ballot(live) != 0 && lane == 0) frow[tm] = 1;
+    }
   }
   if constexpr (sizeof(T) == 2) {
     // Store G in the blocked layout (256 x 32 blocks, see gblock_offset).  One
@@ -706,13 +737,14 @@ __device__ __forceinline__ void replay_epilogue(f32x16_t (&acc)[Geo<T>::TM][Geo<
   }
 }
 
-template <typename T>
+template <typename T, bool FILTER = false>
 __global__ __launch_bounds__(kThreads) void k_replay(
     const T* __restrict__ W, const T* __restrict__ bias, const T* __restrict__ Hc,
     const int* __restrict__ yc, const float* __restrict__ mc, const float* __restrict__ lsc,
     const float* __restrict__ rsc, int Cpad,
     int D, int V, int v0, int vtiles, int tpw, int n_rb, int n_work, int per_xcd, T* __restrict__ Gc,
-    int64_t ldg, float* __restrict__ dbp, int64_t lddb) {
+    int64_t ldg, float* __restrict__ dbp, int64_t lddb, uint8_t* __restrict__ flags = nullptr,
+    int64_t fstride = 0, float eps = 0.f) {
   using C = Cfg<T>;
   using G = Geo<T>;
   extern __shared__ __align__(16) char smem_raw[];
@@ -738,8 +770,8 @@ __global__ __launch_bounds__(kThreads) void k_replay(
           k0 = 0;
         },
         [&](int t, f32x16_t (&acc)[G::TM][G::TN]) {
-          replay_epilogue<T>(acc, bias, v0 + (vt0 + t) * C::BM, n0, V, v0, yc, mc, lsc, rsc, Gc, ldg, dbp, lddb,
-                             rb, red, true, pipe::bias_slice(smem_raw, t));
+          replay_epilogue<T, FILTER>(acc, bias, v0 + (vt0 + t) * C::BM, n0, V, v0, yc, mc, lsc, rsc, Gc, ldg, dbp,
+                                     lddb, rb, red, true, pipe::bias_slice(smem_raw, t), flags, fstride, eps);
         },
         true, reinterpret_cast<const uint16_t*>(bias), V);
   } else {
@@ -755,6 +787,49 @@ __global__ __launch_bounds__(kThreads) void k_replay(
       __syncthreads();  // the next tile's loads reuse the LDS the db sums used
     }
   }
+}
+
+// Stage lists of the gradient filter live in LDS after the pipeline's bytes.
+constexpr int kFilterListCap = 3584;  // entries (14 KB) + 8 wave sums
+constexpr int kFilterLdsBytes = (kFilterListCap + 8) * 4;
+// k_grad's dynamic LDS: the BK=32 pipeline, plus the filter's stage list (bf16).
+template <typename T> constexpr int grad_lds_bytes() {
+  return sizeof(T) == 2 ? pipe32::LDS_BYTES + kFilterLdsBytes : Geo<T>::LDS_BYTES;
+}
+static_assert(pipe32::LDS_BYTES + kFilterLdsBytes <= 160 * 1024, "LDS of one workgroup per CU");
+
+// Compacts {i < n : live(i)} in ascending order into list, each i expanded
+// to `expand` consecutive stages i*expand + 0..expand-1; returns the number
+// of stages, or -1 (list untouched beyond capacity: run every stage) if they
+// would not fit.  All threads of the workgroup call it (it synchronises).
+template <typename Live>
+__device__ int build_live_list(int n, Live live, int* list, int* wsum, int expand) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int total = 0;
+  bool overflow = false;
+  for (int base = 0; base < n; base += kThreads) {
+    const int i = base + (int)threadIdx.x;
+    const bool f = i < n && live(i);
+    const unsigned long long mask = __ballot(f);
+    const int rank = __popcll(mask & ((1ull << lane) - 1ull));
+    if (lane == 0) wsum[wave] = __popcll(mask);
+    __syncthreads();
+    int off = 0, tot = 0;
+#pragma unroll
+    for (int q = 0; q < kThreads / 64; ++q) {
+      off += q < wave ? wsum[q] : 0;
+      tot += wsum[q];
+    }
+    if (f) {
+      const int pos = (total + off + rank) * expand;
+      if (pos + expand <= kFilterListCap)
+        for (int e = 0; e < expand; ++e) list[pos + e] = i * expand + e;
+    }
+    total += tot;
+    overflow = overflow || total * expand > kFilterListCap;
+    __syncthreads();
+  }
+  return overflow ? -1 : total * expand;
 }
 
 // ============================================================== K5 gradients
@@ -803,7 +878,7 @@ __global__ __launch_bounds__(kThreads) void k_grad(
     const T* __restrict__ Gc, int64_t ldg, int kpad_g, const T* __restrict__ Hc,
     const T* __restrict__ W, int Cpad, int D, int v0, int vc, int w_rows, int n_nt, int n_dh_mt, int ks_len,
     int n_dh, int n_dw_mt, int dh_first, float* __restrict__ slots, int64_t slot_stride,
-    int accumulate, T* __restrict__ dW) {
+    int accumulate, T* __restrict__ dW, const uint8_t* __restrict__ flags = nullptr, int64_t fstride = 0) {
   using C = Cfg<T>;
   using G = Geo<T>;
   extern __shared__ __align__(16) char smem_raw[];
@@ -863,10 +938,33 @@ __global__ __launch_bounds__(kThreads) void k_grad(
       k0 = kb;
     };
     auto no_epi = [](int, f32x16_t (&)[G::TM][G::TN]) {};
+    const int kend = nsteps * C::BK;
+    const int* kmap = nullptr;
+    if (flags != nullptr) {
+      // Gradient filtering: run only the stages whose G blocks are live.
+      // dH tile: stage s is G block (row block m0/256, column block kb/32 + s).
+      // dW tile: the 8 stages of row block q cover G blocks (q, m0/32 + 0..7).
+      int* list = reinterpret_cast<int*>(smem_raw + pipe32::LDS_BYTES);
+      int* wsum = list + kFilterListCap;
+      const uint8_t* frow = flags + (int64_t)(m0 / C::BM) * fstride;
+      int n_live;
+      if (dh)
+        n_live = build_live_list(nsteps, [&](int st) { return frow[kb / C::BK + st] != 0; }, list, wsum, 1);
+      else
+        n_live = build_live_list(Cpad / C::BN, [&](int q) {
+          const uint32_t* f = reinterpret_cast<const uint32_t*>(flags + (int64_t)q * fstride + m0 / C::BK);
+          return (f[0] | f[1]) != 0u;
+        }, list, wsum, C::BN / C::BK);
+      if (n_live >= 0) {
+        nsteps = n_live;
+        kmap = list;
+      }
+      if (nsteps == 0) pipe32::zero(acc);
+    }
     if (dh)
-      pipe32::run<0, false>(1, nsteps, nsteps * C::BK, smem_raw, acc, origin, no_epi);
+      pipe32::run<0, false>(1, nsteps, kend, smem_raw, acc, origin, no_epi, true, nullptr, 0, kmap);
     else
-      pipe32::run<1, false>(1, nsteps, nsteps * C::BK, smem_raw, acc, origin, no_epi);
+      pipe32::run<1, false>(1, nsteps, kend, smem_raw, acc, origin, no_epi, true, nullptr, 0, kmap);
     grad_store<T>(acc, dh, m0, n0, D, vc, v0, slot, accumulate, dW);
   } else {
     T* smem = reinterpret_cast<T*>(smem_raw);

@@ -218,10 +218,13 @@ __device__ __forceinline__ void zero(f32x16_t (&acc)[TM][TN]) {
 // right before that tile's first stage: the stage wait that publishes the
 // stage publishes the slice too.  A slot is reloaded 4 tiles later, after the
 // barrier that follows the last epilogue that read it ((4-1)*nsteps >= 3).
+// kmap (optional, LDS, single-tile runs): the stages to run, as indices of
+// BK-wide k steps from k0; stage s loads k = k0 + kmap[s]*BK (the other
+// steps are skipped, as if their operand tiles were zero).
 template <int A_MODE, bool B_KC, int EPI_STORES = 0, typename Origin, typename Epi>
 __device__ __forceinline__ void run(int ntiles, int nsteps, int kend, char* lds, f32x16_t (&acc)[TM][TN],
                                     Origin origin, Epi epi, bool a_kc = true,
-                                    const uint16_t* bias = nullptr, int V = 0) {
+                                    const uint16_t* bias = nullptr, int V = 0, const int* kmap = nullptr) {
   static_assert(BK == 32, "Frags covers the two 16-wide k-substeps of a stage");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave % WGM, wn = wave / WGM;
@@ -250,11 +253,12 @@ __device__ __forceinline__ void run(int ntiles, int nsteps, int kend, char* lds,
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(lds + BIAS_OFFSET + (it & (BIAS_SLOTS - 1)) * BIAS_SLOT_BYTES),
                                                16, (uint32_t)lane * 16, 0, 0, 0);
     }
-    if constexpr (A_MODE == 0) issue_plan<true>(pA, is * BK, kend, st, wave_s);
-    else if constexpr (A_MODE == 1) issue_plan<false>(pA, is * BK, kend, st, wave_s);
-    else if (a_kc) issue_plan<true>(pA, is * BK, kend, st, wave_s);
-    else issue_plan<false>(pA, is * BK, kend, st, wave_s);
-    issue_plan<B_KC>(pB, is * BK, kend, st + OPND_BYTES, wave_s);
+    const int kr = (kmap ? __builtin_amdgcn_readfirstlane(kmap[is]) : is) * BK;
+    if constexpr (A_MODE == 0) issue_plan<true>(pA, kr, kend, st, wave_s);
+    else if constexpr (A_MODE == 1) issue_plan<false>(pA, kr, kend, st, wave_s);
+    else if (a_kc) issue_plan<true>(pA, kr, kend, st, wave_s);
+    else issue_plan<false>(pA, kr, kend, st, wave_s);
+    issue_plan<B_KC>(pB, kr, kend, st + OPND_BYTES, wave_s);
     if (++is == nsteps) {
       is = 0;
       if (++it < ntiles) plan_tile(it);

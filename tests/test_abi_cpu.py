@@ -104,6 +104,15 @@ def test_host_argument_checks_return_before_any_hip_call(lib):
     assert lib.lce_forward_shard(*args, 1, 2, 8, 8, 0, 1, None, None, 0, None) == _lib.LCE_ERR_ARG
     assert lib.lce_backward_shard(*args, 1, 2, 8, 8, -1, 1, 0, None, 0.0, None, None, None, None, None, None,
                                   None, 0, None) == _lib.LCE_ERR_ARG
+    # gradient filter: eps negative / NaN / inf, unknown reduction -> ERR_ARG; fp32 -> UNSUPPORTED
+    bf = lib.lce_backward_filtered
+    for bad in (-1.0, float("nan"), float("inf")):
+        assert bf(*args, 1, 2, 8, 8, 1, 0, None, 0.0, None, None, None, bad, None, None, None, None, 0,
+                  None) == _lib.LCE_ERR_ARG
+    assert bf(*args, 1, 2, 8, 8, 1, 5, None, 0.0, None, None, None, 0.1, None, None, None, None, 0,
+              None) == _lib.LCE_ERR_ARG
+    assert bf(*args, 1, 2, 8, 8, _lib.LCE_DTYPE_F32, 0, None, 0.0, None, None, None, 0.1, None, None, None, None,
+              0, None) == _lib.LCE_ERR_UNSUPPORTED
     # profiling switch validates its argument
     assert lib.lce_profile_start(0) == _lib.LCE_ERR_ARG
     assert lib.lce_profile_count() >= 0
@@ -111,5 +120,6 @@ def test_host_argument_checks_return_before_any_hip_call(lib):
 
 def test_python_binding_names_match_c_abi():
     for n in ("lce_workspace_size", "lce_compact_valid", "lce_forward", "lce_backward", "lce_forward_ex",
-              "lce_backward_ex", "lce_forward_shard", "lce_merge_shards", "lce_backward_shard"):
+              "lce_backward_ex", "lce_backward_filtered", "lce_forward_shard", "lce_merge_shards",
+              "lce_backward_shard"):
         assert callable(getattr(_lib, n))

@@ -1,0 +1,147 @@
+"""Gradient filtering (lce_backward_filtered) against the oracle's
+filtered_backward, through the C ABI.
+
+The filter decides per block (256 supervised rows x 32 vocabulary entries)
+from probabilities, so where a block's largest p sits close to eps the
+float32 kernel and the float64 oracle could decide differently.  The tests
+therefore take eps inside a wide gap of the oracle's block maxima (at least
+a factor 4 from every block), where both sides decide alike, plus eps = 0
+(nothing dropped: bitwise the unfiltered backward) and eps > 1 (only blocks
+holding a target survive).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from lm_head_projection_amd import _lib
+from lm_head_projection_amd import workloads as WL
+
+from lce_harness import assert_grad_close, run_gpu, say, tol, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def peaked_workload(seed=7, N=700, D=128, V=3001):
+    """A bf16 workload with three probability levels set by the bias: targets
+    in [0, 512) (b = +4), a middle band [512, 1024) (b = +1.5) and the rest
+    (b = -2.5); small scores (w_scale 0.02) keep each level tight, so the
+    target-free blocks of the two lower bands sit about e^4 apart."""
+    wl = WL.make_random(N, D, V, dtype=torch.bfloat16, seed=seed, ignore_frac=0.15, mask_frac=0.05,
+                        w_scale=0.02, b_scale=0.05)
+    b = wl.b.float()
+    b[:512] += 4.0
+    b[512:1024] += 1.5
+    b[1024:] -= 2.5
+    wl.b = b.to(torch.bfloat16)
+    g = torch.Generator().manual_seed(seed + 1)
+    keep = wl.labels != wl.ignore_index
+    wl.labels[keep] = torch.randint(0, 512, (int(keep.sum()),), generator=g)
+    return wl
+
+
+def block_maxima(wl, f):
+    """Largest p of every (256-row, 32-column) block without a target (oracle)."""
+    H, W = wl.H.double().numpy(), wl.W.double().numpy()
+    b = None if wl.b is None else wl.b.double().numpy()
+    y = wl.labels.numpy()
+    out = []
+    for lo in range(0, f.C, 256):
+        rows = f.idx[lo:lo + 256]
+        P = np.exp((O.logits(H[rows], W, b) - f.m[rows][:, None]) - f.logs[rows][:, None])
+        for v0 in range(0, wl.V, 32):
+            if not np.any((y[rows] >= v0) & (y[rows] < v0 + 32)):
+                out.append(P[:, v0:v0 + 32].max())
+    return np.array(out)
+
+
+def gap_eps(maxima, factor=4.0):
+    v = np.unique(maxima[maxima > 0])
+    ratios = v[1:] / v[:-1]
+    k = int(np.argmax(ratios))
+    assert ratios[k] >= factor * factor, f"no gap of {factor}x on both sides (best {ratios[k]:.2f})"
+    return float(np.sqrt(v[k] * v[k + 1])), int(k + 1), v.size
+
+
+def run_filtered(wl, eps, dev="cuda:0"):
+    H = wl.H.to(dev)
+    W = wl.W.to(dev)
+    b = None if wl.b is None else wl.b.to(dev)
+    labels = wl.labels.to(dev)
+    mask = None if wl.mask is None else wl.mask.to(torch.uint8).to(dev)
+    N, D = H.shape
+    V = W.shape[0]
+    ws = torch.empty(_lib.lce_workspace_size(N, D, V, H.dtype), dtype=torch.uint8, device=dev)
+    idx = torch.empty(max(N, 1), dtype=torch.int32, device=dev)
+    st, C = _lib.lce_compact_valid(labels, mask, V, wl.ignore_index, idx, ws)
+    assert st == _lib.LCE_OK
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    m = torch.empty(N, dtype=torch.float32, device=dev)
+    logs = torch.empty(N, dtype=torch.float32, device=dev)
+    assert _lib.lce_forward(H, W, b, labels, idx, C, loss, m, logs, None, ws) == _lib.LCE_OK
+    dH = torch.full_like(H, 7.0)
+    dW = torch.full_like(W, 7.0)
+    db = None if b is None else torch.full_like(b, 7.0)
+    g = torch.ones(1, dtype=torch.float32, device=dev)
+    st = _lib.lce_backward_filtered(H, W, b, labels, idx, C, _lib.LCE_REDUCTION_MEAN, None, 0.0, m, logs, g, eps,
+                                    dH, dW, db, ws)
+    torch.cuda.synchronize()
+    return st, to_np(dH), to_np(dW), to_np(db)
+
+
+def oracle_filtered(wl, eps):
+    H, W = wl.H.double().numpy(), wl.W.double().numpy()
+    b = None if wl.b is None else wl.b.double().numpy()
+    mask = None if wl.mask is None else wl.mask.numpy()
+    f = O.dense_forward(H, W, b, wl.labels.numpy(), mask)
+    return f, O.filtered_backward(H, W, b, wl.labels.numpy(), f.m, f.logs, eps, 1.0, mask)
+
+
+@pytest.mark.parametrize("seed", [7, 8])
+def test_filtered_matches_oracle_in_a_gap(seed):
+    wl = peaked_workload(seed)
+    H, W = wl.H.double().numpy(), wl.W.double().numpy()
+    b = None if wl.b is None else wl.b.double().numpy()
+    mask = None if wl.mask is None else wl.mask.numpy()
+    f = O.dense_forward(H, W, b, wl.labels.numpy(), mask)
+    eps, dropped, total = gap_eps(block_maxima(wl, f))
+    say(f"[filter] seed {seed}: eps {eps:.3e} drops {dropped} of {total} target-free blocks")
+    assert 0 < dropped < total
+    g = O.filtered_backward(H, W, b, wl.labels.numpy(), f.m, f.logs, eps, 1.0, mask)
+    gx = O.dense_backward(H, W, b, wl.labels.numpy(), f.m, f.logs, 1.0, mask)
+    st, dH, dW, db = run_filtered(wl, eps)
+    assert st == _lib.LCE_OK, _lib.status_string(st)
+    t = tol(wl.dtype)
+    assert_grad_close("dH filtered", dH, g.dH, t["grad"])
+    assert_grad_close("dW filtered", dW, g.dW, t["grad"])
+    # the filter really dropped something: dW rows of dropped blocks differ from the exact ones
+    assert np.max(np.abs(g.dW - gx.dW)) > 0.0
+
+
+def test_filter_eps_zero_is_bitwise_the_unfiltered_backward():
+    wl = peaked_workload(9)
+    r = run_gpu(wl)
+    st, dH, dW, db = run_filtered(wl, 0.0)
+    assert st == _lib.LCE_OK
+    np.testing.assert_array_equal(dH, r.dH)
+    np.testing.assert_array_equal(dW, r.dW)
+
+
+@pytest.mark.parametrize("name", ["page2_small", "sft_small"])
+def test_filter_huge_eps_keeps_target_blocks_only(name):
+    wl = WL.make_workload(name)
+    f, g = oracle_filtered(wl, 10.0)
+    st, dH, dW, db = run_filtered(wl, 10.0)
+    assert st == _lib.LCE_OK
+    t = tol(wl.dtype)
+    assert_grad_close("dH", dH, g.dH, t["grad"])
+    assert_grad_close("dW", dW, g.dW, t["grad"])
+    if wl.b is not None:
+        assert_grad_close("db (exact)", db, g.db, t["grad"])
+
+
+def test_filter_rejects_fp32_and_bad_eps():
+    wl = WL.make_workload("tiny")
+    st, *_ = run_filtered(wl, 1e-3)
+    assert st == _lib.LCE_ERR_UNSUPPORTED
