@@ -250,7 +250,8 @@ def dense_backward(H, W, b, labels, m, logs, lam: float = 1.0, mask=None,
 
 def filtered_backward(H, W, b, labels, m, logs, eps: float, lam: float = 1.0, mask=None,
                       ignore_index: int = IGNORE_INDEX, row_block: int = 256,
-                      col_block: int = 32) -> BackwardResult:
+                      col_block: int = 32,
+                      row_factor: Optional[np.ndarray] = None) -> BackwardResult:
     """Gradient filtering of small-probability blocks (the CCE threshold
     filter that glenzli.com section 07 describes as an approximation of the
     full gradient).  Reading of the pages: the supervised rows, in ascending
@@ -258,7 +259,10 @@ def filtered_backward(H, W, b, labels, m, logs, eps: float, lam: float = 1.0, ma
     vocabulary into blocks of `col_block` entries; a block whose
     probabilities p_ij are all below `eps` and which holds no row's target
     column contributes nothing to dH and dW.  db keeps every contribution.
-    eps = 0 keeps every block (the exact gradient).
+    eps = 0 keeps every block (the exact gradient).  Rows are scaled by
+    lam / C, or by row_factor[i] (from row_factors) when it is given; a row
+    whose factor is 0 has a zero gradient row, and its probabilities keep no
+    block alive (its target column still does).
     """
     H = _f64(H)
     W = _f64(W)
@@ -273,20 +277,21 @@ def filtered_backward(H, W, b, labels, m, logs, eps: float, lam: float = 1.0, ma
     db = np.zeros(V)
     if C == 0:
         return BackwardResult(dH, dW, db)
-    scale = lam / C
+    r = np.full(N, lam / C) if row_factor is None else np.asarray(row_factor, dtype=np.float64)
     for lo in range(0, C, row_block):
         rows = idx[lo:lo + row_block]
         Z = logits(H[rows], W, b)
         P = np.exp((Z - m[rows][:, None]) - logs[rows][:, None])
         G = P.copy()
         G[np.arange(rows.size), y[rows]] -= 1.0
-        G *= scale
+        G *= r[rows][:, None]
         db += G.sum(axis=0)
         keep = np.zeros_like(G)
+        weighted = r[rows] != 0.0
         for v0 in range(0, V, col_block):
             v1 = min(V, v0 + col_block)
             has_target = np.any((y[rows] >= v0) & (y[rows] < v1))
-            if has_target or np.max(P[:, v0:v1]) >= eps:
+            if has_target or (np.any(weighted) and np.max(P[weighted, v0:v1]) >= eps):
                 keep[:, v0:v1] = 1.0
         Gf = G * keep
         dH[rows] = Gf @ W

@@ -561,3 +561,44 @@ def test_filter_huge_eps_keeps_only_target_blocks():
     # and those blocks keep their exact contribution (every row's whole block)
     f2, g2 = O.dense_forward_backward(H, W, b, y)
     np.testing.assert_allclose(gf.dW[live], g2.dW[live], rtol=1e-12, atol=1e-15)
+
+
+def test_filter_with_row_factors():
+    """Per-row factors (sum with weights, none with per-position upstream
+    values): eps = 0 gives dense_backward with the same factors exactly; at a
+    finite eps every dropped entry is below eps * |r_i| in |G|, so the dH
+    error in row i is at most eps * |r_i| * sum_j |W_j|; a row
+    whose factor is 0 keeps no block alive by its probabilities."""
+    H, W, b, y = _filter_case()
+    N = H.shape[0]
+    f = O.dense_forward(H, W, b, y)
+    rng = np.random.default_rng(5)
+    w = rng.uniform(0.0, 2.0, N)
+    w[[0, 5, 9]] = 0.0
+    r = O.row_factors(N, f.idx, f.C, "sum", 1.3, w, 17.0)
+    g = O.dense_backward(H, W, b, y, f.m, f.logs, row_factor=r)
+    g0 = O.filtered_backward(H, W, b, y, f.m, f.logs, 0.0, row_block=16, row_factor=r)
+    np.testing.assert_allclose(g0.dH, g.dH, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(g0.dW, g.dW, rtol=1e-12, atol=1e-15)
+    eps = 1e-3
+    ge = O.filtered_backward(H, W, b, y, f.m, f.logs, eps, row_block=16, row_factor=r)
+    bound_h = eps * np.abs(r)[:, None] * np.sum(np.abs(W), axis=0)[None, :]
+    assert np.all(np.abs(ge.dH - g.dH) <= bound_h + 1e-15)
+    np.testing.assert_allclose(ge.db, g.db, rtol=1e-12, atol=1e-15)
+    assert np.max(np.abs(ge.dW - g.dW)) > 0
+    # one supervised row with factor 1, all others 0, and a row block holding
+    # everything: the kept blocks are exactly those where that row's p >= eps
+    # or some supervised label falls
+    i = int(f.idx[4])
+    r1 = np.zeros(N)
+    r1[i] = 1.0
+    g1 = O.filtered_backward(H, W, b, y, f.m, f.logs, eps, row_block=1000, row_factor=r1)
+    p = np.exp(O.logits(H[i:i + 1], W, b)[0] - f.m[i] - f.logs[i])
+    Vn = W.shape[0]
+    for v0 in range(0, Vn, 32):
+        live = np.max(p[v0:v0 + 32]) >= eps or np.any((y[f.idx] >= v0) & (y[f.idx] < v0 + 32))
+        Gi = p[v0:v0 + 32].copy()
+        if v0 <= y[i] < v0 + 32:
+            Gi[y[i] - v0] -= 1.0
+        want = np.outer(Gi, H[i]) if live else np.zeros((Gi.size, H.shape[1]))
+        np.testing.assert_allclose(g1.dW[v0:v0 + 32], want, rtol=1e-12, atol=1e-15)
