@@ -41,7 +41,7 @@ def _check(st: int, where: str, allow_empty: bool = True):
 
 class LinearCrossEntropyFunction(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, H, W, b, labels, mask, ignore_index, reduction, loss_weights, num_label_tokens):
+    def forward(ctx, H, W, b, labels, mask, ignore_index, reduction, loss_weights, num_label_tokens, filter_eps):
         H = H.contiguous()
         W = W.contiguous()
         b = None if b is None else b.contiguous()
@@ -60,6 +60,7 @@ class LinearCrossEntropyFunction(torch.autograd.Function):
         _check(st, "lce_forward_ex")
         ctx.s = s
         ctx.red, ctx.w, ctx.num = red, w, num
+        ctx.filter_eps = filter_eps
         ctx.save_for_backward(H, W, b, labels)
         ctx.has_bias = b is not None
         return out.clone() if red == _lib.LCE_REDUCTION_NONE else out[0].clone()
@@ -72,17 +73,23 @@ class LinearCrossEntropyFunction(torch.autograd.Function):
         dW = torch.empty_like(W)
         db = torch.empty_like(b) if ctx.has_bias else None
         g = grad.reshape(-1).to(torch.float32).contiguous()
-        st = _lib.lce_backward_ex(H, W, b, labels, s.valid_idx, s.C, ctx.red, ctx.w, ctx.num, s.m, s.logs,
-                                  g, dH, dW, db, s.ws)
-        _check(st, "lce_backward_ex")
-        return dH, dW, db, None, None, None, None, None, None
+        if ctx.filter_eps is None:
+            st = _lib.lce_backward_ex(H, W, b, labels, s.valid_idx, s.C, ctx.red, ctx.w, ctx.num, s.m, s.logs,
+                                      g, dH, dW, db, s.ws)
+            _check(st, "lce_backward_ex")
+        else:
+            st = _lib.lce_backward_filtered(H, W, b, labels, s.valid_idx, s.C, ctx.red, ctx.w, ctx.num, s.m,
+                                            s.logs, g, ctx.filter_eps, dH, dW, db, s.ws)
+            _check(st, "lce_backward_filtered")
+        return dH, dW, db, None, None, None, None, None, None, None
 
 
 def linear_cross_entropy(hidden: torch.Tensor, weight: torch.Tensor, labels: torch.Tensor,
                          bias: Optional[torch.Tensor] = None, mask: Optional[torch.Tensor] = None,
                          ignore_index: int = IGNORE_INDEX, reduction: str = "mean",
                          loss_weights: Optional[torch.Tensor] = None,
-                         num_label_tokens: Optional[float] = None) -> torch.Tensor:
+                         num_label_tokens: Optional[float] = None,
+                         filter_eps: Optional[float] = None) -> torch.Tensor:
     """CE of (hidden @ weight.T + bias) over supervised rows without forming the logits.
 
     hidden [N, D], weight [V, D], bias [V] (optional), labels [N] (int),
@@ -91,6 +98,10 @@ def linear_cross_entropy(hidden: torch.Tensor, weight: torch.Tensor, labels: tor
     loss_weights [N] and divided by num_label_tokens) or "none" (per-position
     losses [N], 0 on unsupervised positions).  With no supervised rows the
     loss is 0 and every gradient is exactly 0.
+    filter_eps (bf16 only): the backward drops the dH/dW contribution of every
+    block of 256 supervised rows x 32 vocabulary entries that holds no target
+    and whose probabilities are all below filter_eps (an approximation of the
+    gradient; db stays exact).  None or 0 gives the exact gradient.
     """
     if hidden.dim() != 2:
         lead = labels.shape
@@ -101,7 +112,7 @@ def linear_cross_entropy(hidden: torch.Tensor, weight: torch.Tensor, labels: tor
         if loss_weights is not None:
             loss_weights = loss_weights.reshape(-1)
         out = LinearCrossEntropyFunction.apply(hidden, weight, bias, labels, mask, ignore_index, reduction,
-                                               loss_weights, num_label_tokens)
+                                               loss_weights, num_label_tokens, filter_eps)
         return out.reshape(lead) if reduction == "none" else out
     return LinearCrossEntropyFunction.apply(hidden, weight, bias, labels, mask, ignore_index, reduction,
-                                           loss_weights, num_label_tokens)
+                                           loss_weights, num_label_tokens, filter_eps)

@@ -41,8 +41,9 @@ def peaked_workload(seed=7, N=700, D=128, V=3001):
     return wl
 
 
-def block_maxima(wl, f):
-    """Largest p of every (256-row, 32-column) block without a target (oracle)."""
+def block_maxima(wl, f, r=None):
+    """Largest p of every (256-row, 32-column) block without a target (oracle),
+    over the rows whose factor r_i is not 0 (all rows when r is None)."""
     H, W = wl.H.double().numpy(), wl.W.double().numpy()
     b = None if wl.b is None else wl.b.double().numpy()
     y = wl.labels.numpy()
@@ -50,8 +51,10 @@ def block_maxima(wl, f):
     for lo in range(0, f.C, 256):
         rows = f.idx[lo:lo + 256]
         P = np.exp((O.logits(H[rows], W, b) - f.m[rows][:, None]) - f.logs[rows][:, None])
+        if r is not None:
+            P = P[r[rows] != 0.0]
         for v0 in range(0, wl.V, 32):
-            if not np.any((y[rows] >= v0) & (y[rows] < v0 + 32)):
+            if P.shape[0] and not np.any((y[rows] >= v0) & (y[rows] < v0 + 32)):
                 out.append(P[:, v0:v0 + 32].max())
     return np.array(out)
 
@@ -64,7 +67,7 @@ def gap_eps(maxima, factor=4.0):
     return float(np.sqrt(v[k] * v[k + 1])), int(k + 1), v.size
 
 
-def run_filtered(wl, eps, dev="cuda:0"):
+def run_filtered(wl, eps, reduction="mean", weights=None, num=0.0, grad=None, dev="cuda:0"):
     H = wl.H.to(dev)
     W = wl.W.to(dev)
     b = None if wl.b is None else wl.b.to(dev)
@@ -83,8 +86,9 @@ def run_filtered(wl, eps, dev="cuda:0"):
     dH = torch.full_like(H, 7.0)
     dW = torch.full_like(W, 7.0)
     db = None if b is None else torch.full_like(b, 7.0)
-    g = torch.ones(1, dtype=torch.float32, device=dev)
-    st = _lib.lce_backward_filtered(H, W, b, labels, idx, C, _lib.LCE_REDUCTION_MEAN, None, 0.0, m, logs, g, eps,
+    g = torch.tensor(np.atleast_1d(np.asarray(1.0 if grad is None else grad, dtype=np.float32)), device=dev)
+    w = None if weights is None else torch.tensor(weights, dtype=torch.float32, device=dev)
+    st = _lib.lce_backward_filtered(H, W, b, labels, idx, C, _lib.REDUCTIONS[reduction], w, num, m, logs, g, eps,
                                     dH, dW, db, ws)
     torch.cuda.synchronize()
     return st, to_np(dH), to_np(dW), to_np(db)
@@ -119,6 +123,42 @@ def test_filtered_matches_oracle_in_a_gap(seed):
     assert np.max(np.abs(g.dW - gx.dW)) > 0.0
 
 
+@pytest.mark.parametrize("reduction", ["sum", "none"])
+def test_filtered_row_factors_match_oracle_in_a_gap(reduction):
+    """Weighted sum (some weights 0) and none (per-position upstream values,
+    some 0 and some negative): rows with factor 0 keep no block alive."""
+    wl = peaked_workload(8)
+    N = wl.N
+    H, W = wl.H.double().numpy(), wl.W.double().numpy()
+    b = None if wl.b is None else wl.b.double().numpy()
+    mask = None if wl.mask is None else wl.mask.numpy()
+    y = wl.labels.numpy()
+    f = O.dense_forward(H, W, b, y, mask)
+    rng = np.random.default_rng(21)
+    if reduction == "sum":
+        weights = rng.uniform(0.2, 2.0, N).astype(np.float32)
+        weights[rng.random(N) < 0.3] = 0.0
+        num, grad = 333.0, 0.75
+        r = O.row_factors(N, f.idx, f.C, "sum", float(np.float32(grad)), weights.astype(np.float64), num)
+    else:
+        weights, num = None, 0.0
+        grad = rng.uniform(-2.0, 2.0, N).astype(np.float32)
+        grad[rng.random(N) < 0.3] = 0.0
+        r = O.row_factors(N, f.idx, f.C, "none", grad.astype(np.float64))
+    eps, dropped, total = gap_eps(block_maxima(wl, f, r))
+    say(f"[filter] {reduction}: eps {eps:.3e} drops {dropped} of {total} target-free blocks")
+    assert 0 < dropped < total
+    g = O.filtered_backward(H, W, b, y, f.m, f.logs, eps, mask=mask, row_factor=r)
+    gx = O.dense_backward(H, W, b, y, f.m, f.logs, mask=mask, row_factor=r)
+    st, dH, dW, db = run_filtered(wl, eps, reduction, weights, num, grad)
+    assert st == _lib.LCE_OK, _lib.status_string(st)
+    t = tol(wl.dtype)
+    assert_grad_close("dH filtered", dH, g.dH, t["grad"])
+    assert_grad_close("dW filtered", dW, g.dW, t["grad"])
+    assert_grad_close("db (exact)", db, g.db, t["grad"])
+    assert np.max(np.abs(g.dW - gx.dW)) > 0.0
+
+
 def test_filter_eps_zero_is_bitwise_the_unfiltered_backward():
     wl = peaked_workload(9)
     r = run_gpu(wl)
@@ -145,3 +185,22 @@ def test_filter_rejects_fp32_and_bad_eps():
     wl = WL.make_workload("tiny")
     st, *_ = run_filtered(wl, 1e-3)
     assert st == _lib.LCE_ERR_UNSUPPORTED
+
+
+def test_autograd_filter_eps_matches_the_entry_point():
+    """linear_cross_entropy(..., filter_eps=e) runs lce_backward_filtered:
+    its gradients equal the entry point's bit for bit (deterministic kernels)."""
+    from lm_head_projection_amd import linear_cross_entropy
+    wl = WL.make_workload("page2_small")
+    dev = "cuda:0"
+    st, dH0, dW0, db0 = run_filtered(wl, 10.0)
+    assert st == _lib.LCE_OK
+    H = wl.H.to(dev).requires_grad_(True)
+    W = wl.W.to(dev).requires_grad_(True)
+    b = wl.b.to(dev).requires_grad_(True)
+    loss = linear_cross_entropy(H, W, wl.labels.to(dev), bias=b, mask=wl.mask.to(dev), filter_eps=10.0)
+    loss.backward()
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_np(H.grad), dH0)
+    np.testing.assert_array_equal(to_np(W.grad), dW0)
+    np.testing.assert_array_equal(to_np(b.grad), db0)
