@@ -251,7 +251,8 @@ def dense_backward(H, W, b, labels, m, logs, lam: float = 1.0, mask=None,
 def filtered_backward(H, W, b, labels, m, logs, eps: float, lam: float = 1.0, mask=None,
                       ignore_index: int = IGNORE_INDEX, row_block: int = 256,
                       col_block: int = 32,
-                      row_factor: Optional[np.ndarray] = None) -> BackwardResult:
+                      row_factor: Optional[np.ndarray] = None,
+                      filter_dh: bool = True, filter_dw: bool = True) -> BackwardResult:
     """Gradient filtering of small-probability blocks (the CCE threshold
     filter that glenzli.com section 07 describes as an approximation of the
     full gradient).  Reading of the pages: the supervised rows, in ascending
@@ -262,7 +263,9 @@ def filtered_backward(H, W, b, labels, m, logs, eps: float, lam: float = 1.0, ma
     eps = 0 keeps every block (the exact gradient).  Rows are scaled by
     lam / C, or by row_factor[i] (from row_factors) when it is given; a row
     whose factor is 0 has a zero gradient row, and its probabilities keep no
-    block alive (its target column still does).
+    block alive (its target column still does).  Section 07 names the
+    embedding-gradient (dH) and classifier-gradient (dW) filters separately;
+    filter_dh / filter_dw switch each one, the other gradient being exact.
     """
     H = _f64(H)
     W = _f64(W)
@@ -294,8 +297,8 @@ def filtered_backward(H, W, b, labels, m, logs, eps: float, lam: float = 1.0, ma
             if has_target or (np.any(weighted) and np.max(P[weighted, v0:v1]) >= eps):
                 keep[:, v0:v1] = 1.0
         Gf = G * keep
-        dH[rows] = Gf @ W
-        dW += Gf.T @ H[rows]
+        dH[rows] = (Gf if filter_dh else G) @ W
+        dW += (Gf if filter_dw else G).T @ H[rows]
     return BackwardResult(dH, dW, db)
 
 

@@ -602,3 +602,19 @@ def test_filter_with_row_factors():
             Gi[y[i] - v0] -= 1.0
         want = np.outer(Gi, H[i]) if live else np.zeros((Gi.size, H.shape[1]))
         np.testing.assert_allclose(g1.dW[v0:v0 + 32], want, rtol=1e-12, atol=1e-15)
+
+
+def test_filter_one_gradient_at_a_time():
+    """Filtering only dH leaves dW exactly the dense one, and the reverse;
+    the filtered gradient equals the one filtered together with the other."""
+    H, W, b, y = _filter_case()
+    f, g = O.dense_forward_backward(H, W, b, y)
+    eps = 1e-3
+    both = O.filtered_backward(H, W, b, y, f.m, f.logs, eps, row_block=16)
+    only_h = O.filtered_backward(H, W, b, y, f.m, f.logs, eps, row_block=16, filter_dw=False)
+    only_w = O.filtered_backward(H, W, b, y, f.m, f.logs, eps, row_block=16, filter_dh=False)
+    np.testing.assert_allclose(only_h.dW, g.dW, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(only_w.dH, g.dH, rtol=1e-12, atol=1e-15)
+    np.testing.assert_array_equal(only_h.dH, both.dH)
+    np.testing.assert_array_equal(only_w.dW, both.dW)
+    assert np.max(np.abs(only_h.dH - g.dH)) > 0 and np.max(np.abs(only_w.dW - g.dW)) > 0
