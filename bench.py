@@ -45,6 +45,8 @@ def parse():
     p.add_argument("--shards", type=int, default=8, help="vocabulary shards for --mode shard")
     p.add_argument("--filter-eps", type=float, default=None,
                    help="train with the gradient filter at this threshold (lce_backward_filtered)")
+    p.add_argument("--filter-grads", choices=["dh", "dw", "both"], default="both",
+                   help="which gradients the filter applies to")
     p.add_argument("--reduction", choices=("mean", "sum", "none"), default="mean",
                    help="mean: plain entries; sum (per-position weights, divisor N) / none: the _ex entries")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -231,7 +233,8 @@ def main():
             return C
         if args.filter_eps is not None:
             st = _lib.lce_backward_filtered(H, W, b, labels, idx, C, red, weights, num, m, logs, grad,
-                                            args.filter_eps, dH, dW, db, ws, stream)
+                                            args.filter_eps, dH, dW, db, ws, stream,
+                                            which={"dh": 1, "dw": 2, "both": 3}[args.filter_grads])
         elif plain:
             st = _lib.lce_backward(H, W, b, labels, idx, C, m, logs, grad, dH, dW, db, ws, stream)
         else:
@@ -322,7 +325,8 @@ def main():
         "config": {"workload": args.workload, "N": N, "D": D, "V": V, "C": C,
                    "bias": b is not None, "mask": mask is not None, "mode": args.mode,
                    "reduction": args.reduction, "shards": args.shards if args.mode == "shard" else 1,
-                   "filter_eps": args.filter_eps},
+                   "filter_eps": args.filter_eps,
+                   "filter_grads": args.filter_grads if args.filter_eps is not None else None},
         "tflops": tflops,
         "pct_peak": 100.0 * tflops / peak,
         "positions_per_s": N * args.steps / (total_ms * 1e-3),

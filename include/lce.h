@@ -164,21 +164,33 @@ lce_status_t lce_backward_ex(const void* H, const void* W, const void* b, const 
                              const float* grad_loss, void* dH, void* dW, void* db, void* ws,
                              size_t ws_bytes, void* stream);
 
+/* Which gradients lce_backward_filtered filters.  The glenzli.com page,
+ * section 07, names the two filters of CCE separately: the embedding
+ * gradient (dH) and the classifier gradient (dW), each of which an exact
+ * variant turns off. */
+typedef enum {
+  LCE_FILTER_DH = 1,   /* embedding gradient only; dW exact */
+  LCE_FILTER_DW = 2,   /* classifier gradient only; dH exact */
+  LCE_FILTER_BOTH = 3
+} lce_filter_t;
+
 /* Backward with gradient filtering (the threshold filter of CCE that the
  * glenzli.com page, section 07, describes as an approximation of the full
  * gradient): the supervised rows, in ascending position order, are cut into
  * blocks of 256 and the vocabulary into blocks of 32; a block of G in which
- * every entry has |r_i| p_ij < eps |r_i| (or r_i = 0) and which holds no
- * row's target column is skipped by the dH and dW products.  db keeps every
- * contribution.  eps = 0 skips only blocks of exact zeros.  bf16 only
- * (LCE_ERR_UNSUPPORTED for fp32); eps must be finite and >= 0.  Other
- * arguments as for lce_backward_ex. */
+ * every entry of a row with r_i != 0 has p_ij < eps, and which holds no
+ * row's target column, is skipped by the products that `which` selects
+ * (dH, dW or both).  db keeps every contribution.  eps = 0 skips only blocks
+ * of exact zeros, so the result is that of lce_backward_ex bit for bit.
+ * bf16 only (LCE_ERR_UNSUPPORTED for fp32); eps must be finite and >= 0 and
+ * `which` one of lce_filter_t (else LCE_ERR_ARG).  Other arguments as for
+ * lce_backward_ex. */
 lce_status_t lce_backward_filtered(const void* H, const void* W, const void* b, const int64_t* labels,
                                    const int32_t* valid_idx, int64_t C, int64_t N, int64_t D, int64_t V,
                                    lce_dtype_t dt, lce_reduction_t reduction, const float* loss_weights,
                                    double num_label_tokens, const float* m, const float* logs,
-                                   const float* grad_loss, float eps, void* dH, void* dW, void* db, void* ws,
-                                   size_t ws_bytes, void* stream);
+                                   const float* grad_loss, float eps, int32_t which, void* dH, void* dW,
+                                   void* db, void* ws, size_t ws_bytes, void* stream);
 
 /* ---- Vocabulary sharding on one device --------------------------------------
  * The exchange that splitting W over P devices needs (glenzli.com page,

@@ -28,6 +28,9 @@ LCE_ERR_UNSUPPORTED = -5
 LCE_REDUCTION_MEAN = 0
 LCE_REDUCTION_SUM = 1
 LCE_REDUCTION_NONE = 2
+LCE_FILTER_DH = 1
+LCE_FILTER_DW = 2
+LCE_FILTER_BOTH = 3
 REDUCTIONS = {"mean": LCE_REDUCTION_MEAN, "sum": LCE_REDUCTION_SUM, "none": LCE_REDUCTION_NONE}
 
 # Every entry point that include/lce.h declares.
@@ -85,7 +88,7 @@ def load() -> ctypes.CDLL:
                                     ctypes.c_int, vp, dbl, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.lce_backward_ex.restype = ctypes.c_int
     lib.lce_backward_filtered.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int, vp,
-                                          dbl, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, sz, vp]
+                                          dbl, vp, vp, vp, ctypes.c_float, i32, vp, vp, vp, vp, sz, vp]
     lib.lce_backward_filtered.restype = ctypes.c_int
     lib.lce_forward_shard.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int, vp, vp, sz, vp]
     lib.lce_forward_shard.restype = ctypes.c_int
@@ -185,13 +188,16 @@ def lce_backward_ex(H, W, b, labels, valid_idx, C: int, reduction: int, loss_wei
 
 
 def lce_backward_filtered(H, W, b, labels, valid_idx, C: int, reduction: int, loss_weights, num_label_tokens: float,
-                          m, logs, grad_loss, eps: float, dH, dW, db, ws, stream=None) -> int:
+                          m, logs, grad_loss, eps: float, dH, dW, db, ws, stream=None,
+                          which: int = 3) -> int:
+    """which: LCE_FILTER_DH (1), LCE_FILTER_DW (2) or LCE_FILTER_BOTH (3)."""
     N, D = H.shape
     V = W.shape[0]
     return load().lce_backward_filtered(_ptr(H), _ptr(W), _ptr(b), _ptr(labels), _ptr(valid_idx), C, N, D, V,
                                         dtype_code(H.dtype), int(reduction), _ptr(loss_weights),
                                         float(num_label_tokens), _ptr(m), _ptr(logs), _ptr(grad_loss), float(eps),
-                                        _ptr(dH), _ptr(dW), _ptr(db), _ptr(ws), ws.numel(), _stream_ptr(stream))
+                                        int(which), _ptr(dH), _ptr(dW), _ptr(db), _ptr(ws), ws.numel(),
+                                        _stream_ptr(stream))
 
 
 def lce_forward_shard(H, W_shard, b_shard, labels, valid_idx, C: int, v_begin: int, part, ws, stream=None) -> int:

@@ -313,7 +313,7 @@ lce_status_t backward_impl(const T* H, const T* W, const T* b, const int64_t* la
                            const int32_t* idx, int64_t C, int64_t N, int64_t D, int64_t V, int64_t label_off,
                            const Reduce& red, const float* m, const float* logs, const float* grad_loss,
                            T* dH, T* dW, T* db, char* ws, const Layout& L, hipStream_t s,
-                           float filter_eps = -1.f) {
+                           float filter_eps = -1.f, int filter_which = 0) {
   using Cf = Cfg<T>;
   const int Cpad = (int)rup(C, 256);
   T* Hc = reinterpret_cast<T*>(ws + L.hc);
@@ -345,7 +345,7 @@ lce_status_t backward_impl(const T* H, const T* W, const T* b, const int64_t* la
   const int n_rb = Cpad / Cf::BN;
   const int n_nt = (int)cdiv(D, Cf::BN);
   const int n_dh_mt = Cpad / Cf::BM;
-  const bool filter = filter_eps >= 0.f;
+  const bool filter = filter_eps >= 0.f && filter_which != 0;
   uint8_t* flags = filter ? reinterpret_cast<uint8_t*>(ws + L.flags) : nullptr;
   const int64_t fstride = L.Vc / 32;
   set_lds_attr<T>((const void*)k_replay<T, false>, gemm_lds_bytes<T>());
@@ -384,7 +384,8 @@ lce_status_t backward_impl(const T* H, const T* W, const T* b, const int64_t* la
     const int dh_first = ks_len >= Cpad ? 1 : 0;
     LCE_LAUNCH("k_grad", (k_grad<T>), per_xcd * 8, kThreads, grad_lds_bytes<T>(), s, Gc, ldg, kpad, Hc,
                W, Cpad, (int)D, (int)v0, vc, (int)(V - v0), n_nt, n_dh_mt, (int)ks_len, n_dh, vtiles,
-               dh_first, slots, slot_stride, chunk == 0 ? 0 : 1, dW, (const uint8_t*)flags, fstride);
+               dh_first, slots, slot_stride, chunk == 0 ? 0 : 1, dW, (const uint8_t*)flags, fstride,
+               filter_which);
   }
   {
     const int64_t vec = N * (D / 4);
@@ -468,7 +469,8 @@ lce_status_t backward_entry(const void* H, const void* W, const void* b, const i
                             const int32_t* valid_idx, int64_t C, int64_t N, int64_t D, int64_t V,
                             lce_dtype_t dt, const Reduce& red, const float* m, const float* logs,
                             const float* grad_loss, void* dH, void* dW, void* db, void* ws,
-                            size_t ws_bytes, void* stream, int64_t label_off = 0, float filter_eps = -1.f) {
+                            size_t ws_bytes, void* stream, int64_t label_off = 0, float filter_eps = -1.f,
+                            int filter_which = 0) {
   try {
     if (!dims_ok(N, D, V, dt) || C < 0 || C > N) return LCE_ERR_ARG;
     if (!dW || (N > 0 && !dH)) return LCE_ERR_ARG;
@@ -491,7 +493,8 @@ lce_status_t backward_entry(const void* H, const void* W, const void* b, const i
     if (dt == LCE_DTYPE_BF16)
       return backward_impl<uint16_t>((const uint16_t*)H, (const uint16_t*)W, (const uint16_t*)b, labels,
                                      valid_idx, C, N, D, V, label_off, red, m, logs, grad_loss, (uint16_t*)dH,
-                                     (uint16_t*)dW, (uint16_t*)db, w, L, s, filter_eps);
+                                     (uint16_t*)dW, (uint16_t*)db, w, L, s, filter_eps,
+                                     filter_which);
     if (filter_eps >= 0.f) return LCE_ERR_UNSUPPORTED;  // the filter runs on the bf16 path only
     return backward_impl<float>((const float*)H, (const float*)W, (const float*)b, labels, valid_idx, C,
                                 N, D, V, label_off, red, m, logs, grad_loss, (float*)dH, (float*)dW, (float*)db, w,
@@ -675,14 +678,15 @@ lce_status_t lce_backward_filtered(const void* H, const void* W, const void* b, 
                                    const int32_t* valid_idx, int64_t C, int64_t N, int64_t D, int64_t V,
                                    lce_dtype_t dt, lce_reduction_t reduction, const float* loss_weights,
                                    double num_label_tokens, const float* m, const float* logs,
-                                   const float* grad_loss, float eps, void* dH, void* dW, void* db, void* ws,
-                                   size_t ws_bytes, void* stream) {
+                                   const float* grad_loss, float eps, int32_t which, void* dH, void* dW,
+                                   void* db, void* ws, size_t ws_bytes, void* stream) {
   Reduce red;
   LCE_TRY(make_reduce(reduction, loss_weights, num_label_tokens, red));
   if (!(eps >= 0.f) || std::isinf(eps)) return LCE_ERR_ARG;
+  if (which < LCE_FILTER_DH || which > LCE_FILTER_BOTH) return LCE_ERR_ARG;
   if (dt != LCE_DTYPE_BF16) return dims_ok(N, D, V, dt) ? LCE_ERR_UNSUPPORTED : LCE_ERR_ARG;
   return backward_entry(H, W, b, labels, valid_idx, C, N, D, V, dt, red, m, logs, grad_loss, dH, dW, db, ws,
-                        ws_bytes, stream, 0, eps);
+                        ws_bytes, stream, 0, eps, which);
 }
 
 lce_status_t lce_profile_start(int32_t max_launches) {

@@ -878,7 +878,8 @@ __global__ __launch_bounds__(kThreads) void k_grad(
     const T* __restrict__ Gc, int64_t ldg, int kpad_g, const T* __restrict__ Hc,
     const T* __restrict__ W, int Cpad, int D, int v0, int vc, int w_rows, int n_nt, int n_dh_mt, int ks_len,
     int n_dh, int n_dw_mt, int dh_first, float* __restrict__ slots, int64_t slot_stride,
-    int accumulate, T* __restrict__ dW, const uint8_t* __restrict__ flags = nullptr, int64_t fstride = 0) {
+    int accumulate, T* __restrict__ dW, const uint8_t* __restrict__ flags = nullptr, int64_t fstride = 0,
+    int fmask = 0) {
   using C = Cfg<T>;
   using G = Geo<T>;
   extern __shared__ __align__(16) char smem_raw[];
@@ -940,8 +941,9 @@ __global__ __launch_bounds__(kThreads) void k_grad(
     auto no_epi = [](int, f32x16_t (&)[G::TM][G::TN]) {};
     const int kend = nsteps * C::BK;
     const int* kmap = nullptr;
-    if (flags != nullptr) {
-      // Gradient filtering: run only the stages whose G blocks are live.
+    if (flags != nullptr && (fmask & (dh ? 1 : 2)) != 0) {
+      // Gradient filtering (fmask bit 0: dH items, bit 1: dW items): run only
+      // the stages whose G blocks are live.
       // dH tile: stage s is G block (row block m0/256, column block kb/32 + s).
       // dW tile: the 8 stages of row block q cover G blocks (q, m0/32 + 0..7).
       int* list = reinterpret_cast<int*>(smem_raw + pipe32::LDS_BYTES);

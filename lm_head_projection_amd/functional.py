@@ -13,6 +13,7 @@ import torch
 from . import _lib
 
 IGNORE_INDEX = -100
+_FILTERS = {"dh": _lib.LCE_FILTER_DH, "dw": _lib.LCE_FILTER_DW, "both": _lib.LCE_FILTER_BOTH}
 
 
 class Saved:
@@ -41,7 +42,8 @@ def _check(st: int, where: str, allow_empty: bool = True):
 
 class LinearCrossEntropyFunction(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, H, W, b, labels, mask, ignore_index, reduction, loss_weights, num_label_tokens, filter_eps):
+    def forward(ctx, H, W, b, labels, mask, ignore_index, reduction, loss_weights, num_label_tokens, filter_eps,
+                filter_grads):
         H = H.contiguous()
         W = W.contiguous()
         b = None if b is None else b.contiguous()
@@ -61,6 +63,7 @@ class LinearCrossEntropyFunction(torch.autograd.Function):
         ctx.s = s
         ctx.red, ctx.w, ctx.num = red, w, num
         ctx.filter_eps = filter_eps
+        ctx.filter_which = _FILTERS[filter_grads]
         ctx.save_for_backward(H, W, b, labels)
         ctx.has_bias = b is not None
         return out.clone() if red == _lib.LCE_REDUCTION_NONE else out[0].clone()
@@ -79,9 +82,9 @@ class LinearCrossEntropyFunction(torch.autograd.Function):
             _check(st, "lce_backward_ex")
         else:
             st = _lib.lce_backward_filtered(H, W, b, labels, s.valid_idx, s.C, ctx.red, ctx.w, ctx.num, s.m,
-                                            s.logs, g, ctx.filter_eps, dH, dW, db, s.ws)
+                                            s.logs, g, ctx.filter_eps, dH, dW, db, s.ws, which=ctx.filter_which)
             _check(st, "lce_backward_filtered")
-        return dH, dW, db, None, None, None, None, None, None, None
+        return dH, dW, db, None, None, None, None, None, None, None, None
 
 
 def linear_cross_entropy(hidden: torch.Tensor, weight: torch.Tensor, labels: torch.Tensor,
@@ -89,7 +92,7 @@ def linear_cross_entropy(hidden: torch.Tensor, weight: torch.Tensor, labels: tor
                          ignore_index: int = IGNORE_INDEX, reduction: str = "mean",
                          loss_weights: Optional[torch.Tensor] = None,
                          num_label_tokens: Optional[float] = None,
-                         filter_eps: Optional[float] = None) -> torch.Tensor:
+                         filter_eps: Optional[float] = None, filter_grads: str = "both") -> torch.Tensor:
     """CE of (hidden @ weight.T + bias) over supervised rows without forming the logits.
 
     hidden [N, D], weight [V, D], bias [V] (optional), labels [N] (int),
@@ -102,7 +105,11 @@ def linear_cross_entropy(hidden: torch.Tensor, weight: torch.Tensor, labels: tor
     block of 256 supervised rows x 32 vocabulary entries that holds no target
     and whose probabilities are all below filter_eps (an approximation of the
     gradient; db stays exact).  None or 0 gives the exact gradient.
+    filter_grads: "both", "dh" (the embedding gradient only; dW exact) or
+    "dw" (the classifier gradient only; dH exact).
     """
+    if filter_grads not in _FILTERS:
+        raise ValueError(f"filter_grads must be one of {sorted(_FILTERS)}")
     if hidden.dim() != 2:
         lead = labels.shape
         hidden = hidden.reshape(-1, hidden.shape[-1])
@@ -112,7 +119,7 @@ def linear_cross_entropy(hidden: torch.Tensor, weight: torch.Tensor, labels: tor
         if loss_weights is not None:
             loss_weights = loss_weights.reshape(-1)
         out = LinearCrossEntropyFunction.apply(hidden, weight, bias, labels, mask, ignore_index, reduction,
-                                               loss_weights, num_label_tokens, filter_eps)
+                                               loss_weights, num_label_tokens, filter_eps, filter_grads)
         return out.reshape(lead) if reduction == "none" else out
     return LinearCrossEntropyFunction.apply(hidden, weight, bias, labels, mask, ignore_index, reduction,
-                                           loss_weights, num_label_tokens, filter_eps)
+                                           loss_weights, num_label_tokens, filter_eps, filter_grads)

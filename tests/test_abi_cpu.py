@@ -107,12 +107,15 @@ def test_host_argument_checks_return_before_any_hip_call(lib):
     # gradient filter: eps negative / NaN / inf, unknown reduction -> ERR_ARG; fp32 -> UNSUPPORTED
     bf = lib.lce_backward_filtered
     for bad in (-1.0, float("nan"), float("inf")):
-        assert bf(*args, 1, 2, 8, 8, 1, 0, None, 0.0, None, None, None, bad, None, None, None, None, 0,
+        assert bf(*args, 1, 2, 8, 8, 1, 0, None, 0.0, None, None, None, bad, 3, None, None, None, None, 0,
                   None) == _lib.LCE_ERR_ARG
-    assert bf(*args, 1, 2, 8, 8, 1, 5, None, 0.0, None, None, None, 0.1, None, None, None, None, 0,
+    assert bf(*args, 1, 2, 8, 8, 1, 5, None, 0.0, None, None, None, 0.1, 3, None, None, None, None, 0,
               None) == _lib.LCE_ERR_ARG
-    assert bf(*args, 1, 2, 8, 8, _lib.LCE_DTYPE_F32, 0, None, 0.0, None, None, None, 0.1, None, None, None, None,
-              0, None) == _lib.LCE_ERR_UNSUPPORTED
+    for which in (0, 4, -1):
+        assert bf(*args, 1, 2, 8, 8, 1, 0, None, 0.0, None, None, None, 0.1, which, None, None, None, None, 0,
+                  None) == _lib.LCE_ERR_ARG
+    assert bf(*args, 1, 2, 8, 8, _lib.LCE_DTYPE_F32, 0, None, 0.0, None, None, None, 0.1, 3, None, None, None,
+              None, 0, None) == _lib.LCE_ERR_UNSUPPORTED
     # profiling switch validates its argument
     assert lib.lce_profile_start(0) == _lib.LCE_ERR_ARG
     assert lib.lce_profile_count() >= 0

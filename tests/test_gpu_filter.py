@@ -67,7 +67,7 @@ def gap_eps(maxima, factor=4.0):
     return float(np.sqrt(v[k] * v[k + 1])), int(k + 1), v.size
 
 
-def run_filtered(wl, eps, reduction="mean", weights=None, num=0.0, grad=None, dev="cuda:0"):
+def run_filtered(wl, eps, reduction="mean", weights=None, num=0.0, grad=None, which=3, dev="cuda:0"):
     H = wl.H.to(dev)
     W = wl.W.to(dev)
     b = None if wl.b is None else wl.b.to(dev)
@@ -89,7 +89,7 @@ def run_filtered(wl, eps, reduction="mean", weights=None, num=0.0, grad=None, de
     g = torch.tensor(np.atleast_1d(np.asarray(1.0 if grad is None else grad, dtype=np.float32)), device=dev)
     w = None if weights is None else torch.tensor(weights, dtype=torch.float32, device=dev)
     st = _lib.lce_backward_filtered(H, W, b, labels, idx, C, _lib.REDUCTIONS[reduction], w, num, m, logs, g, eps,
-                                    dH, dW, db, ws)
+                                    dH, dW, db, ws, which=which)
     torch.cuda.synchronize()
     return st, to_np(dH), to_np(dW), to_np(db)
 
@@ -157,6 +157,33 @@ def test_filtered_row_factors_match_oracle_in_a_gap(reduction):
     assert_grad_close("dW filtered", dW, g.dW, t["grad"])
     assert_grad_close("db (exact)", db, g.db, t["grad"])
     assert np.max(np.abs(g.dW - gx.dW)) > 0.0
+
+
+@pytest.mark.parametrize("which", [_lib.LCE_FILTER_DH, _lib.LCE_FILTER_DW])
+def test_filter_one_gradient_keeps_the_other_exact(which):
+    """The embedding-gradient (dH) and classifier-gradient (dW) filters
+    apart: the filtered one matches the oracle, the other is bitwise the
+    unfiltered backward's."""
+    wl = peaked_workload(7)
+    H, W = wl.H.double().numpy(), wl.W.double().numpy()
+    b = None if wl.b is None else wl.b.double().numpy()
+    mask = None if wl.mask is None else wl.mask.numpy()
+    f = O.dense_forward(H, W, b, wl.labels.numpy(), mask)
+    eps, _, _ = gap_eps(block_maxima(wl, f))
+    fdh, fdw = which == _lib.LCE_FILTER_DH, which == _lib.LCE_FILTER_DW
+    g = O.filtered_backward(H, W, b, wl.labels.numpy(), f.m, f.logs, eps, 1.0, mask, filter_dh=fdh,
+                            filter_dw=fdw)
+    r = run_gpu(wl)
+    st, dH, dW, db = run_filtered(wl, eps, which=which)
+    assert st == _lib.LCE_OK
+    t = tol(wl.dtype)
+    if fdh:
+        assert_grad_close("dH filtered", dH, g.dH, t["grad"])
+        np.testing.assert_array_equal(dW, r.dW)
+    else:
+        assert_grad_close("dW filtered", dW, g.dW, t["grad"])
+        np.testing.assert_array_equal(dH, r.dH)
+    np.testing.assert_array_equal(db, r.db)
 
 
 def test_filter_eps_zero_is_bitwise_the_unfiltered_backward():
