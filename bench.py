@@ -45,7 +45,7 @@ def parse():
     p.add_argument("--shards", type=int, default=8, help="vocabulary shards for --mode shard")
     p.add_argument("--filter-eps", type=float, default=None,
                    help="train with the gradient filter at this threshold (lce_backward_filtered)")
-    p.add_argument("--filter-grads", choices=["dh", "dw", "both"], default="both",
+    p.add_argument("--filter-grads", choices=["dh", "both"], default="both",
                    help="which gradients the filter applies to")
     p.add_argument("--reduction", choices=("mean", "sum", "none"), default="mean",
                    help="mean: plain entries; sum (per-position weights, divisor N) / none: the _ex entries")
@@ -234,7 +234,7 @@ def main():
         if args.filter_eps is not None:
             st = _lib.lce_backward_filtered(H, W, b, labels, idx, C, red, weights, num, m, logs, grad,
                                             args.filter_eps, dH, dW, db, ws, stream,
-                                            which={"dh": 1, "dw": 2, "both": 3}[args.filter_grads])
+                                            which={"dh": 1, "both": 3}[args.filter_grads])
         elif plain:
             st = _lib.lce_backward(H, W, b, labels, idx, C, m, logs, grad, dH, dW, db, ws, stream)
         else:

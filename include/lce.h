@@ -165,13 +165,12 @@ lce_status_t lce_backward_ex(const void* H, const void* W, const void* b, const 
                              size_t ws_bytes, void* stream);
 
 /* Which gradients lce_backward_filtered filters.  The glenzli.com page,
- * section 07, names the two filters of CCE separately: the embedding
- * gradient (dH) and the classifier gradient (dW), each of which an exact
- * variant turns off. */
+ * section 07, names CCE's embedding-gradient (dH) and classifier-gradient
+ * (dW) filters and the variants that turn off the classifier filter, or
+ * both (the exact gradient: lce_backward_ex). */
 typedef enum {
   LCE_FILTER_DH = 1,   /* embedding gradient only; dW exact */
-  LCE_FILTER_DW = 2,   /* classifier gradient only; dH exact */
-  LCE_FILTER_BOTH = 3
+  LCE_FILTER_BOTH = 3  /* embedding and classifier gradients */
 } lce_filter_t;
 
 /* Backward with gradient filtering (the threshold filter of CCE that the
@@ -180,7 +179,7 @@ typedef enum {
  * blocks of 256 and the vocabulary into blocks of 32; a block of G in which
  * every entry of a row with r_i != 0 has p_ij < eps, and which holds no
  * row's target column, is skipped by the products that `which` selects
- * (dH, dW or both).  db keeps every contribution.  eps = 0 skips only blocks
+ * (dH, or dH and dW).  db keeps every contribution.  eps = 0 skips only blocks
  * of exact zeros, so the result is that of lce_backward_ex bit for bit.
  * bf16 only (LCE_ERR_UNSUPPORTED for fp32); eps must be finite and >= 0 and
  * `which` one of lce_filter_t (else LCE_ERR_ARG).  Other arguments as for

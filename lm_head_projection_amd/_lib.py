@@ -29,7 +29,6 @@ LCE_REDUCTION_MEAN = 0
 LCE_REDUCTION_SUM = 1
 LCE_REDUCTION_NONE = 2
 LCE_FILTER_DH = 1
-LCE_FILTER_DW = 2
 LCE_FILTER_BOTH = 3
 REDUCTIONS = {"mean": LCE_REDUCTION_MEAN, "sum": LCE_REDUCTION_SUM, "none": LCE_REDUCTION_NONE}
 
@@ -190,7 +189,7 @@ def lce_backward_ex(H, W, b, labels, valid_idx, C: int, reduction: int, loss_wei
 def lce_backward_filtered(H, W, b, labels, valid_idx, C: int, reduction: int, loss_weights, num_label_tokens: float,
                           m, logs, grad_loss, eps: float, dH, dW, db, ws, stream=None,
                           which: int = 3) -> int:
-    """which: LCE_FILTER_DH (1), LCE_FILTER_DW (2) or LCE_FILTER_BOTH (3)."""
+    """which: LCE_FILTER_DH (1: dH filtered, dW exact) or LCE_FILTER_BOTH (3)."""
     N, D = H.shape
     V = W.shape[0]
     return load().lce_backward_filtered(_ptr(H), _ptr(W), _ptr(b), _ptr(labels), _ptr(valid_idx), C, N, D, V,

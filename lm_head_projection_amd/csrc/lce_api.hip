@@ -349,7 +349,7 @@ lce_status_t backward_impl(const T* H, const T* W, const T* b, const int64_t* la
   uint8_t* flags = filter ? reinterpret_cast<uint8_t*>(ws + L.flags) : nullptr;
   const int64_t fstride = L.Vc / 32;
   set_lds_attr<T>((const void*)k_replay<T, false>, gemm_lds_bytes<T>());
-  set_lds_attr<T>((const void*)k_replay<T, true>, gemm_lds_bytes<T>());
+  set_lds_attr<T>((const void*)k_replay<T, true>, replay_lds_bytes<T, true>());
   set_lds_attr<T>((const void*)k_grad<T>, grad_lds_bytes<T>());
 
   int S = 0;  // dH k-splits, fixed by the first (widest) chunk
@@ -363,14 +363,15 @@ lce_status_t backward_impl(const T* H, const T* W, const T* b, const int64_t* la
       const int n_work = n_rb * (int)cdiv(vtiles, tpw);
       const int per_xcd = (int)cdiv(n_work, 8);
       if (filter) {
-        LCE_TRY(zero_bytes(flags, (int64_t)n_rb * fstride, s));
-        LCE_LAUNCH("k_replay", (k_replay<T, true>), per_xcd * 8, kThreads, gemm_lds_bytes<T>(), s, W, b, Hc,
+        // Every flag of the chunk's tiles is written (0 or 1) by the tile's replay.
+        LCE_LAUNCH("k_replay", (k_replay<T, true>), per_xcd * 8, kThreads, (replay_lds_bytes<T, true>()), s, W, b, Hc,
                    yc, mc, lsc, rsc, Cpad, (int)D, (int)V, (int)v0, vtiles, tpw, n_rb, n_work, per_xcd, Gc, ldg,
-                   db ? dbp : (float*)nullptr, lddb, flags, fstride, filter_eps);
+                   db ? dbp : (float*)nullptr, lddb, flags, fstride, filter_eps,
+                   filter_which == LCE_FILTER_BOTH ? 1 : 0);
       } else {
         LCE_LAUNCH("k_replay", (k_replay<T, false>), per_xcd * 8, kThreads, gemm_lds_bytes<T>(), s, W, b, Hc,
                    yc, mc, lsc, rsc, Cpad, (int)D, (int)V, (int)v0, vtiles, tpw, n_rb, n_work, per_xcd, Gc, ldg,
-                   db ? dbp : (float*)nullptr, lddb, (uint8_t*)nullptr, (int64_t)0, 0.f);
+                   db ? dbp : (float*)nullptr, lddb, (uint8_t*)nullptr, (int64_t)0, 0.f, 0);
       }
     }
     // K5: dH split so that one dH tile's K matches one dW tile's K (= Cpad).
@@ -683,7 +684,7 @@ lce_status_t lce_backward_filtered(const void* H, const void* W, const void* b, 
   Reduce red;
   LCE_TRY(make_reduce(reduction, loss_weights, num_label_tokens, red));
   if (!(eps >= 0.f) || std::isinf(eps)) return LCE_ERR_ARG;
-  if (which < LCE_FILTER_DH || which > LCE_FILTER_BOTH) return LCE_ERR_ARG;
+  if (which != LCE_FILTER_DH && which != LCE_FILTER_BOTH) return LCE_ERR_ARG;
   if (dt != LCE_DTYPE_BF16) return dims_ok(N, D, V, dt) ? LCE_ERR_UNSUPPORTED : LCE_ERR_ARG;
   return backward_entry(H, W, b, labels, valid_idx, C, N, D, V, dt, red, m, logs, grad_loss, dH, dW, db, ws,
                         ws_bytes, stream, 0, eps, which);

@@ -401,6 +401,11 @@ __global__ __launch_bounds__(kThreads) void k_fwd(const T* __restrict__ W, const
 template <typename T> constexpr int gemm_lds_bytes() {
   return sizeof(T) == 2 ? pipe::LDS_BYTES : Geo<T>::LDS_BYTES;
 }
+// The filtered replay adds one vote word per wave after the pipeline's bytes.
+constexpr int kVoteBytes = pipe::NWAVES * 4;
+template <typename T, bool FILTER> constexpr int replay_lds_bytes() {
+  return gemm_lds_bytes<T>() + (FILTER ? kVoteBytes : 0);
+}
 
 // ============================================================== K3 merge + loss
 // Per supervised row: merge the split partials in split order (online-softmax
@@ -561,7 +566,8 @@ __device__ __forceinline__ void replay_epilogue(f32x16_t (&acc)[Geo<T>::TM][Geo<
                                                 int rb, float* red, bool raw_sync,
                                                 const uint16_t* bias_slice = nullptr,
                                                 uint8_t* __restrict__ flags = nullptr, int64_t fstride = 0,
-                                                float eps = 0.f) {
+                                                float eps = 0.f, uint32_t* votes = nullptr,
+                                                int zero_dead = 0) {
   using C = Cfg<T>;
   using G = Geo<T>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -626,10 +632,17 @@ __device__ __forceinline__ void replay_epilogue(f32x16_t (&acc)[Geo<T>::TM][Geo<
 #pragma unroll
           for (int tn = 0; tn < G::TN; ++tn) acc[tm][tn][i] = 0.f;
   }
+  // Filter blocks kept (bit tm: column block tm of this wave).  When dW is
+  // filtered too (zero_dead), dead blocks are stored as exact zeros: a dW
+  // k-step covers all 8 column blocks of a tile, and must sum the live ones
+  // only.  (A dH k-step is exactly one block, so dH needs no zeros.)  The
+  // db sums below use the unmasked values.
+  uint32_t keep = ~0u;
   if constexpr (FILTER) {
-    // Block (row block n0/256, chunk column block (vbase - v0)/32 + tm):
-    // every wave holding part of it votes; any live entry marks it (the
-    // marks of different waves all write 1).  Ragged columns are 0 here.
+    // Block (row block n0/256, chunk column block (vbase - v0)/32 + tm): its
+    // 256 rows lie in the WGN waves with this wm.  Each wave votes on its
+    // rows, the votes meet in LDS, and the wn == 0 wave writes the flag (one
+    // writer per flag, 0 or 1).  Ragged columns are 0 here.
     float thr[G::TN];  // eps |r|, or +inf for rows with r = 0 (never live)
     int dd[G::TN];
 #pragma unroll
@@ -639,7 +652,7 @@ __device__ __forceinline__ void replay_epilogue(f32x16_t (&acc)[Geo<T>::TM][Geo<
       thr[tn] = ar > 0.f ? eps * ar : INFINITY;
       dd[tn] = yc[r] - vbase;
     }
-    uint8_t* frow = flags + (int64_t)(n0 / C::BN) * fstride + (vbase - v0) / 32;
+    uint32_t mine = 0;
 #pragma unroll
     for (int tm = 0; tm < G::TM; ++tm) {
       bool live = false;
@@ -649,8 +662,17 @@ __device__ __forceinline__ void replay_epilogue(f32x16_t (&acc)[Geo<T>::TM][Geo<
 #pragma unroll
         for (int i = 0; i < 16; ++i) live = live || fabsf(acc[tm][tn][i]) >= thr[tn];
       }
-      if (__ballot(live) != 0 && lane == 0) frow[tm] = 1;
+      if (__ballot(live) != 0) mine |= 1u << tm;
     }
+    if (lane == 0) votes[wave] = mine;
+    pipe::wait_lgkm0();
+    pipe::raw_barrier();
+    uint32_t live = 0;
+#pragma unroll
+    for (int q = 0; q < G::WGN; ++q) live |= votes[q * G::WGM + wm];
+    if (wn == 0 && lane < G::TM)
+      flags[(int64_t)(n0 / C::BN) * fstride + (vbase - v0) / 32 + lane] = (uint8_t)((live >> lane) & 1u);
+    if (zero_dead) keep = live;
   }
   if constexpr (sizeof(T) == 2) {
     // Store G in the blocked layout (256 x 32 blocks, see gblock_offset).  One
@@ -668,11 +690,13 @@ __device__ __forceinline__ void replay_epilogue(f32x16_t (&acc)[Geo<T>::TM][Geo<
 #pragma unroll
       for (int tm = 0; tm < G::TM; ++tm) {
         uint32_t d[8];
+        const uint32_t km = ((keep >> tm) & 1u) ? ~0u : 0u;
 #pragma unroll
         for (int k = 0; k < 8; ++k)
-          d[k] = ((uint32_t)from_f32<uint16_t>(acc[tm][tn][2 * k]) |
-                  ((uint32_t)from_f32<uint16_t>(acc[tm][tn][2 * k + 1]) << 16)) ^
-                 smask[tn];
+          d[k] = (((uint32_t)from_f32<uint16_t>(acc[tm][tn][2 * k]) |
+                   ((uint32_t)from_f32<uint16_t>(acc[tm][tn][2 * k + 1]) << 16)) ^
+                  smask[tn]) &
+                 km;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           // lanes 32..63 of d[k] <-> lanes 0..31 of d[k + 4]
@@ -744,7 +768,7 @@ __global__ __launch_bounds__(kThreads) void k_replay(
     const float* __restrict__ rsc, int Cpad,
     int D, int V, int v0, int vtiles, int tpw, int n_rb, int n_work, int per_xcd, T* __restrict__ Gc,
     int64_t ldg, float* __restrict__ dbp, int64_t lddb, uint8_t* __restrict__ flags = nullptr,
-    int64_t fstride = 0, float eps = 0.f) {
+    int64_t fstride = 0, float eps = 0.f, int zero_dead = 0) {
   using C = Cfg<T>;
   using G = Geo<T>;
   extern __shared__ __align__(16) char smem_raw[];
@@ -771,7 +795,8 @@ __global__ __launch_bounds__(kThreads) void k_replay(
         },
         [&](int t, f32x16_t (&acc)[G::TM][G::TN]) {
           replay_epilogue<T, FILTER>(acc, bias, v0 + (vt0 + t) * C::BM, n0, V, v0, yc, mc, lsc, rsc, Gc, ldg, dbp,
-                                     lddb, rb, red, true, pipe::bias_slice(smem_raw, t), flags, fstride, eps);
+                                     lddb, rb, red, true, pipe::bias_slice(smem_raw, t), flags, fstride, eps,
+                                     reinterpret_cast<uint32_t*>(smem_raw + pipe::LDS_BYTES), zero_dead);
         },
         true, reinterpret_cast<const uint16_t*>(bias), V);
   } else {

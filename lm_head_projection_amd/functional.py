@@ -13,7 +13,7 @@ import torch
 from . import _lib
 
 IGNORE_INDEX = -100
-_FILTERS = {"dh": _lib.LCE_FILTER_DH, "dw": _lib.LCE_FILTER_DW, "both": _lib.LCE_FILTER_BOTH}
+_FILTERS = {"dh": _lib.LCE_FILTER_DH, "both": _lib.LCE_FILTER_BOTH}
 
 
 class Saved:
@@ -105,8 +105,7 @@ def linear_cross_entropy(hidden: torch.Tensor, weight: torch.Tensor, labels: tor
     block of 256 supervised rows x 32 vocabulary entries that holds no target
     and whose probabilities are all below filter_eps (an approximation of the
     gradient; db stays exact).  None or 0 gives the exact gradient.
-    filter_grads: "both", "dh" (the embedding gradient only; dW exact) or
-    "dw" (the classifier gradient only; dH exact).
+    filter_grads: "both", or "dh" (the embedding gradient only; dW exact).
     """
     if filter_grads not in _FILTERS:
         raise ValueError(f"filter_grads must be one of {sorted(_FILTERS)}")

@@ -248,6 +248,16 @@ def dense_backward(H, W, b, labels, m, logs, lam: float = 1.0, mask=None,
     return BackwardResult(dH, dW, db)
 
 
+def _block_kept(P_block, y_rows, r_rows, v0: int, v1: int, eps: float) -> bool:
+    """The filter's decision for one block (rows y_rows, columns [v0, v1),
+    probabilities P_block): kept if some row's target column lies in it, or
+    if some row with a non-zero factor has p >= eps there."""
+    if np.any((y_rows >= v0) & (y_rows < v1)):
+        return True
+    weighted = r_rows != 0.0
+    return bool(np.any(weighted) and np.max(P_block[weighted]) >= eps)
+
+
 def filtered_backward(H, W, b, labels, m, logs, eps: float, lam: float = 1.0, mask=None,
                       ignore_index: int = IGNORE_INDEX, row_block: int = 256,
                       col_block: int = 32,
@@ -290,16 +300,74 @@ def filtered_backward(H, W, b, labels, m, logs, eps: float, lam: float = 1.0, ma
         G *= r[rows][:, None]
         db += G.sum(axis=0)
         keep = np.zeros_like(G)
-        weighted = r[rows] != 0.0
         for v0 in range(0, V, col_block):
             v1 = min(V, v0 + col_block)
-            has_target = np.any((y[rows] >= v0) & (y[rows] < v1))
-            if has_target or (np.any(weighted) and np.max(P[weighted, v0:v1]) >= eps):
+            if _block_kept(P[:, v0:v1], y[rows], r[rows], v0, v1, eps):
                 keep[:, v0:v1] = 1.0
         Gf = G * keep
         dH[rows] = (Gf if filter_dh else G) @ W
         dW += (Gf if filter_dw else G).T @ H[rows]
     return BackwardResult(dH, dW, db)
+
+
+def filtered_rows_grad(H, W, b, labels, m, logs, eps: float, rows, cols, lam: float = 1.0, mask=None,
+                       ignore_index: int = IGNORE_INDEX, row_block: int = 256, col_block: int = 32):
+    """Chosen rows of dH (positions `rows`, all supervised) and of dW
+    (vocabulary entries `cols`) of filtered_backward (both gradients
+    filtered, rows scaled by lam / C), for checks at sizes where the whole
+    filtered gradient is out of reach.  Only the row blocks that hold a
+    chosen row, and the column blocks that hold a chosen entry, are
+    projected.  Also returns the decision margin: the smallest
+    |log(max p / eps)| over the blocks decided by probability alone (inf if
+    none), which tells how far every such decision sits from the threshold.
+    """
+    H = _f64(H)
+    W = _f64(W)
+    b = _f64(b)
+    a, idx, C = supervised_rows(labels, mask, ignore_index)
+    check_labels(labels, idx, W.shape[0])
+    y = np.asarray(labels, dtype=np.int64)
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.asarray(cols, dtype=np.int64)
+    assert np.all(a[rows]), "chosen rows must be supervised"
+    rank = np.full(H.shape[0], -1, dtype=np.int64)
+    rank[idx] = np.arange(C)
+    r = np.full(H.shape[0], lam / C)
+    margin = np.inf
+
+    def decide(P_block, blk, v0, v1):
+        nonlocal margin
+        kept = _block_kept(P_block, y[blk], r[blk], v0, v1, eps)
+        if not np.any((y[blk] >= v0) & (y[blk] < v1)) and eps > 0:
+            margin = min(margin, abs(np.log(np.max(P_block) / eps)))
+        return kept
+
+    V = W.shape[0]
+    dH_rows = np.zeros((rows.size, H.shape[1]))
+    for q in np.unique(rank[rows] // row_block):
+        blk = idx[q * row_block:(q + 1) * row_block]
+        P = np.exp((logits(H[blk], W, b) - m[blk][:, None]) - logs[blk][:, None])
+        live = np.zeros(V, dtype=bool)
+        for v0 in range(0, V, col_block):
+            v1 = min(V, v0 + col_block)
+            live[v0:v1] = decide(P[:, v0:v1], blk, v0, v1)
+        for k in np.flatnonzero(rank[rows] // row_block == q):
+            i = int(rank[rows[k]]) - q * row_block
+            g = P[i].copy()
+            g[y[blk[i]]] -= 1.0
+            dH_rows[k] = r[blk[i]] * (np.where(live, g, 0.0) @ W)
+    dW_rows = np.zeros((cols.size, H.shape[1]))
+    for k, v in enumerate(cols):
+        v0 = (int(v) // col_block) * col_block
+        v1 = min(V, v0 + col_block)
+        for lo in range(0, C, row_block):
+            blk = idx[lo:lo + row_block]
+            bb = None if b is None else b[v0:v1]
+            P = np.exp((logits(H[blk], W[v0:v1], bb) - m[blk][:, None]) - logs[blk][:, None])
+            if decide(P, blk, v0, v1):
+                g = P[:, int(v) - v0] - (y[blk] == v)
+                dW_rows[k] += (r[blk] * g) @ H[blk]
+    return dH_rows, dW_rows, margin
 
 
 def dense_forward_backward(H, W, b, labels, mask=None, lam: float = 1.0,

@@ -163,3 +163,33 @@ def run_gpu_ex(wl: Workload, reduction: str, weights=None, num: float = 0.0, gra
         torch.cuda.synchronize()
         r.dH, r.dW, r.db = to_np(dH), to_np(dW), to_np(db)
     return r
+
+
+def run_gpu_filtered(wl: Workload, eps: float, reduction: str = "mean", weights=None, num: float = 0.0,
+                     grad=None, which: int = 3, dev: str = "cuda:0"):
+    """compact -> lce_forward -> lce_backward_filtered through the C ABI.
+    Returns (status, dH, dW, db) as host arrays."""
+    H = wl.H.to(dev)
+    W = wl.W.to(dev)
+    b = None if wl.b is None else wl.b.to(dev)
+    labels = wl.labels.to(dev)
+    mask = None if wl.mask is None else wl.mask.to(torch.uint8).to(dev)
+    N, D = H.shape
+    V = W.shape[0]
+    ws = torch.empty(_lib.lce_workspace_size(N, D, V, H.dtype), dtype=torch.uint8, device=dev)
+    idx = torch.empty(max(N, 1), dtype=torch.int32, device=dev)
+    st, C = _lib.lce_compact_valid(labels, mask, V, wl.ignore_index, idx, ws)
+    assert st == _lib.LCE_OK
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    m = torch.empty(N, dtype=torch.float32, device=dev)
+    logs = torch.empty(N, dtype=torch.float32, device=dev)
+    assert _lib.lce_forward(H, W, b, labels, idx, C, loss, m, logs, None, ws) == _lib.LCE_OK
+    dH = torch.full_like(H, 7.0)
+    dW = torch.full_like(W, 7.0)
+    db = None if b is None else torch.full_like(b, 7.0)
+    g = torch.tensor(np.atleast_1d(np.asarray(1.0 if grad is None else grad, dtype=np.float32)), device=dev)
+    w = None if weights is None else torch.tensor(weights, dtype=torch.float32, device=dev)
+    st = _lib.lce_backward_filtered(H, W, b, labels, idx, C, _lib.REDUCTIONS[reduction], w, num, m, logs, g, eps,
+                                    dH, dW, db, ws, which=which)
+    torch.cuda.synchronize()
+    return st, to_np(dH), to_np(dW), to_np(db)

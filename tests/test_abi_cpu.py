@@ -111,7 +111,7 @@ def test_host_argument_checks_return_before_any_hip_call(lib):
                   None) == _lib.LCE_ERR_ARG
     assert bf(*args, 1, 2, 8, 8, 1, 5, None, 0.0, None, None, None, 0.1, 3, None, None, None, None, 0,
               None) == _lib.LCE_ERR_ARG
-    for which in (0, 4, -1):
+    for which in (0, 2, 4, -1):
         assert bf(*args, 1, 2, 8, 8, 1, 0, None, 0.0, None, None, None, 0.1, which, None, None, None, None, 0,
                   None) == _lib.LCE_ERR_ARG
     assert bf(*args, 1, 2, 8, 8, _lib.LCE_DTYPE_F32, 0, None, 0.0, None, None, None, 0.1, 3, None, None, None,

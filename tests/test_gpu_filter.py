@@ -18,7 +18,7 @@ import oracle as O
 from lm_head_projection_amd import _lib
 from lm_head_projection_amd import workloads as WL
 
-from lce_harness import assert_grad_close, run_gpu, say, tol, to_np
+from lce_harness import assert_grad_close, run_gpu, run_gpu_filtered, say, tol, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -67,31 +67,8 @@ def gap_eps(maxima, factor=4.0):
     return float(np.sqrt(v[k] * v[k + 1])), int(k + 1), v.size
 
 
-def run_filtered(wl, eps, reduction="mean", weights=None, num=0.0, grad=None, which=3, dev="cuda:0"):
-    H = wl.H.to(dev)
-    W = wl.W.to(dev)
-    b = None if wl.b is None else wl.b.to(dev)
-    labels = wl.labels.to(dev)
-    mask = None if wl.mask is None else wl.mask.to(torch.uint8).to(dev)
-    N, D = H.shape
-    V = W.shape[0]
-    ws = torch.empty(_lib.lce_workspace_size(N, D, V, H.dtype), dtype=torch.uint8, device=dev)
-    idx = torch.empty(max(N, 1), dtype=torch.int32, device=dev)
-    st, C = _lib.lce_compact_valid(labels, mask, V, wl.ignore_index, idx, ws)
-    assert st == _lib.LCE_OK
-    loss = torch.empty(1, dtype=torch.float32, device=dev)
-    m = torch.empty(N, dtype=torch.float32, device=dev)
-    logs = torch.empty(N, dtype=torch.float32, device=dev)
-    assert _lib.lce_forward(H, W, b, labels, idx, C, loss, m, logs, None, ws) == _lib.LCE_OK
-    dH = torch.full_like(H, 7.0)
-    dW = torch.full_like(W, 7.0)
-    db = None if b is None else torch.full_like(b, 7.0)
-    g = torch.tensor(np.atleast_1d(np.asarray(1.0 if grad is None else grad, dtype=np.float32)), device=dev)
-    w = None if weights is None else torch.tensor(weights, dtype=torch.float32, device=dev)
-    st = _lib.lce_backward_filtered(H, W, b, labels, idx, C, _lib.REDUCTIONS[reduction], w, num, m, logs, g, eps,
-                                    dH, dW, db, ws, which=which)
-    torch.cuda.synchronize()
-    return st, to_np(dH), to_np(dW), to_np(db)
+def run_filtered(wl, eps, reduction="mean", weights=None, num=0.0, grad=None, which=3):
+    return run_gpu_filtered(wl, eps, reduction, weights, num, grad, which)
 
 
 def oracle_filtered(wl, eps):
@@ -159,31 +136,43 @@ def test_filtered_row_factors_match_oracle_in_a_gap(reduction):
     assert np.max(np.abs(g.dW - gx.dW)) > 0.0
 
 
-@pytest.mark.parametrize("which", [_lib.LCE_FILTER_DH, _lib.LCE_FILTER_DW])
-def test_filter_one_gradient_keeps_the_other_exact(which):
-    """The embedding-gradient (dH) and classifier-gradient (dW) filters
-    apart: the filtered one matches the oracle, the other is bitwise the
-    unfiltered backward's."""
+def test_filter_dh_only_keeps_dw_exact():
+    """The embedding-gradient filter alone (the variant with an exact
+    classifier gradient): dH matches the oracle's filtered dH, dW and db are
+    bitwise the unfiltered backward's."""
     wl = peaked_workload(7)
     H, W = wl.H.double().numpy(), wl.W.double().numpy()
     b = None if wl.b is None else wl.b.double().numpy()
     mask = None if wl.mask is None else wl.mask.numpy()
     f = O.dense_forward(H, W, b, wl.labels.numpy(), mask)
     eps, _, _ = gap_eps(block_maxima(wl, f))
-    fdh, fdw = which == _lib.LCE_FILTER_DH, which == _lib.LCE_FILTER_DW
-    g = O.filtered_backward(H, W, b, wl.labels.numpy(), f.m, f.logs, eps, 1.0, mask, filter_dh=fdh,
-                            filter_dw=fdw)
+    g = O.filtered_backward(H, W, b, wl.labels.numpy(), f.m, f.logs, eps, 1.0, mask, filter_dw=False)
     r = run_gpu(wl)
-    st, dH, dW, db = run_filtered(wl, eps, which=which)
+    st, dH, dW, db = run_filtered(wl, eps, which=_lib.LCE_FILTER_DH)
     assert st == _lib.LCE_OK
     t = tol(wl.dtype)
-    if fdh:
-        assert_grad_close("dH filtered", dH, g.dH, t["grad"])
-        np.testing.assert_array_equal(dW, r.dW)
-    else:
-        assert_grad_close("dW filtered", dW, g.dW, t["grad"])
-        np.testing.assert_array_equal(dH, r.dH)
+    assert_grad_close("dH filtered", dH, g.dH, t["grad"])
+    assert np.max(np.abs(r.dH - dH)) > 0.0
+    np.testing.assert_array_equal(dW, r.dW)
     np.testing.assert_array_equal(db, r.db)
+
+
+def test_filter_mixed_tiles_drop_dead_blocks_exactly():
+    """A 256-wide dW tile whose column blocks are partly live: the dead
+    blocks' rows of dW are exactly 0 (eps > 1 keeps only blocks holding a
+    target), and the live rows match the oracle."""
+    wl = WL.make_workload("sft_small")
+    f, g = oracle_filtered(wl, 10.0)
+    st, dH, dW, db = run_filtered(wl, 10.0)
+    assert st == _lib.LCE_OK
+    y = wl.labels.numpy()
+    live = np.zeros(wl.V, dtype=bool)
+    for lo in range(0, f.C, 256):
+        for lab in y[f.idx[lo:lo + 256]]:
+            live[(lab // 32) * 32:(lab // 32) * 32 + 32] = True
+    assert np.all(dW[~live] == 0.0)
+    t = tol(wl.dtype)
+    assert_grad_close("dW", dW, g.dW, t["grad"])
 
 
 def test_filter_eps_zero_is_bitwise_the_unfiltered_backward():

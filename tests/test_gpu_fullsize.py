@@ -21,7 +21,7 @@ import oracle as O
 from lm_head_projection_amd import _lib
 from lm_head_projection_amd import workloads as WL
 
-from lce_harness import assert_grad_close, assert_stat_close, run_gpu, say, tol
+from lce_harness import assert_grad_close, assert_stat_close, run_gpu, run_gpu_filtered, say, tol
 
 pytestmark = pytest.mark.gpu
 
@@ -144,3 +144,62 @@ def test_fullsize_packed_eight_vocabulary_shards():
     t = tol(wl.dtype)
     assert_grad_close("dW", r1["dW"], r0.dW, t["grad"])
     assert_grad_close("dH", r1["dH"], r0.dH, t["grad"])
+
+
+def test_fullsize_packed_filter_sparse_elementwise():
+    """Gradient filtering at the packed sizes with 48 supervised rows (one
+    row block), eps = 1e-3: every output element against the oracle's
+    filtered backward.  Every block decided by probability sits at least a
+    factor 4 from eps, so both sides decide alike."""
+    wl, Wd, bd = workload("packed")
+    sub = WL.supervised_subset(wl, 48)
+    eps = 1e-3
+    say("[fullsize] packed: filtered backward, 48 supervised rows")
+    st, dH, dW, db = run_gpu_filtered(sub, eps)
+    assert st == _lib.LCE_OK
+    say("[fullsize] packed: oracle filtered backward on the 48 rows")
+    Hd, y, mk = sub.H.double().numpy(), sub.labels.numpy(), sub.mask.numpy()
+    f = O.dense_forward(Hd, Wd, bd, y, mk)
+    g = O.filtered_backward(Hd, Wd, bd, y, f.m, f.logs, eps, 1.0, mk)
+    P = np.exp((O.logits(Hd[f.idx], Wd, bd) - f.m[f.idx][:, None]) - f.logs[f.idx][:, None])
+    P[np.arange(f.C), y[f.idx]] = 0.0
+    tgt = np.zeros(wl.V // 32 + 1, dtype=bool)
+    tgt[y[f.idx] // 32] = True
+    blk_max = np.max(P[:, :(wl.V // 32) * 32].reshape(f.C, -1, 32), axis=(0, 2))
+    free = blk_max[~tgt[:blk_max.size]]
+    assert np.all(np.abs(np.log(free / eps)) > np.log(4.0))
+    t = tol(wl.dtype)
+    assert_grad_close("dH filtered", dH, g.dH, t["grad"])
+    assert_grad_close("dW filtered", dW, g.dW, t["grad"])
+    assert np.count_nonzero(np.any(dW != 0.0, axis=1)) <= 32 * int(tgt.sum())
+
+
+def test_fullsize_packed_filter_keeps_target_blocks():
+    """Full supervision at the packed sizes, eps = 10 (above every p): only
+    blocks holding a target survive.  dW rows of vocabulary blocks that hold
+    no label are exactly 0; sampled dH rows of the first and the last
+    (ragged) row block against the oracle's filtered rows."""
+    wl, Wd, bd = workload("packed")
+    say("[fullsize] packed: filtered backward, eps 10")
+    st, dH, dW, db = run_gpu_filtered(wl, 10.0)
+    assert st == _lib.LCE_OK
+    y = wl.labels.numpy()
+    _, idx, C = O.supervised_rows(y, None)
+    labelled = np.zeros(wl.V // 32 + 1, dtype=bool)
+    labelled[y[idx] // 32] = True
+    dead = ~labelled[np.arange(wl.V) // 32]
+    assert np.all(dW[dead] == 0.0)
+    last = (C - 1) // 256
+    blocks = np.concatenate([idx[:256], idx[last * 256:]])
+    rng = np.random.default_rng(29)
+    rows = np.unique(np.concatenate([idx[[0, 255, last * 256, C - 1]],
+                                     rng.choice(idx[:256], 2, replace=False),
+                                     rng.choice(idx[last * 256:], 2, replace=False)]))
+    say(f"[fullsize] packed: oracle statistics of {blocks.size} rows, filtered dH of {rows.size}")
+    sel = np.zeros(wl.N, dtype=bool)
+    sel[blocks] = True
+    Hd = wl.H.double().numpy()
+    f = O.dense_forward(Hd, Wd, bd, y, sel)
+    dh, _, _ = O.filtered_rows_grad(Hd, Wd, bd, y, f.m, f.logs, 10.0, rows, [], 1.0)
+    t = tol(wl.dtype)
+    assert_grad_close("dH rows filtered", dH[rows], dh, t["grad"])

@@ -618,3 +618,21 @@ def test_filter_one_gradient_at_a_time():
     np.testing.assert_array_equal(only_h.dH, both.dH)
     np.testing.assert_array_equal(only_w.dW, both.dW)
     assert np.max(np.abs(only_h.dH - g.dH)) > 0 and np.max(np.abs(only_w.dW - g.dW)) > 0
+
+
+def test_filtered_rows_grad_equals_the_whole_filtered_gradient():
+    """The sampled-row form picks the same rows out of filtered_backward, at
+    a finite eps (some blocks dropped) and with ragged row and column blocks;
+    its decision margin is the distance of the closest block maximum."""
+    H, W, b, y = _filter_case(N=70, V=203)
+    f = O.dense_forward(H, W, b, y)
+    eps, lam = 1e-3, 0.8
+    g = O.filtered_backward(H, W, b, y, f.m, f.logs, eps, lam, row_block=16)
+    rows = f.idx[[0, 5, 17, 31, -1]]
+    cols = np.array([0, 31, 64, 100, 202])
+    dh, dw, margin = O.filtered_rows_grad(H, W, b, y, f.m, f.logs, eps, rows, cols, lam, row_block=16)
+    np.testing.assert_allclose(dh, g.dH[rows], rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(dw, g.dW[cols], rtol=1e-12, atol=1e-15)
+    assert 0 < margin < np.inf
+    gx = O.dense_backward(H, W, b, y, f.m, f.logs, lam)
+    assert np.max(np.abs(g.dW[cols] - gx.dW[cols])) > 0
