@@ -226,12 +226,17 @@ int choose_dh_splits(int64_t kpad, int64_t Cpad, int64_t Npad, int64_t n_dh_tile
 
 // Vocabulary tiles per replay workgroup: minimise (waves of workgroups) x
 // (tiles per workgroup) with at most 8 tiles, ties to fewer tiles.
-int choose_tiles_per_wg(int n_rb, int vtiles) {
+// Replay tiles per workgroup: minimises the makespan in pipeline stages,
+// waves * (tpw * nsteps + kItemStages), where kItemStages stands for the
+// per-workgroup cost the tile walk cannot hide (the first stages' load
+// latency and the last tile's epilogue).
+constexpr int kItemStages = 3;
+int choose_tiles_per_wg(int n_rb, int vtiles, int nsteps) {
   int best = 1;
   int64_t best_cost = INT64_MAX;
   for (int tpw = 1; tpw <= std::min(vtiles, 8); ++tpw) {
     const int64_t waves = cdiv((int64_t)n_rb * cdiv(vtiles, tpw), kCUs);
-    const int64_t cost = waves * tpw;
+    const int64_t cost = waves * ((int64_t)tpw * nsteps + kItemStages);
     if (cost < best_cost) {
       best_cost = cost;
       best = tpw;
@@ -348,7 +353,7 @@ lce_status_t backward_impl(const T* H, const T* W, const T* b, const int64_t* la
   const bool filter = filter_eps >= 0.f && filter_which != 0;
   uint8_t* flags = filter ? reinterpret_cast<uint8_t*>(ws + L.flags) : nullptr;
   const int64_t fstride = L.Vc / 32;
-  set_lds_attr<T>((const void*)k_replay<T, false>, gemm_lds_bytes<T>());
+  set_lds_attr<T>((const void*)k_replay<T, false>, replay_lds_bytes<T, false>());
   set_lds_attr<T>((const void*)k_replay<T, true>, replay_lds_bytes<T, true>());
   set_lds_attr<T>((const void*)k_grad<T>, grad_lds_bytes<T>());
 
@@ -359,7 +364,7 @@ lce_status_t backward_impl(const T* H, const T* W, const T* b, const int64_t* la
     const int kpad = vtiles * Cf::BM;
     // K4: replay this chunk into G.
     {
-      const int tpw = choose_tiles_per_wg(n_rb, vtiles);
+      const int tpw = choose_tiles_per_wg(n_rb, vtiles, (int)cdiv(D, sizeof(T) == 2 ? 64 : Cf::BK));
       const int n_work = n_rb * (int)cdiv(vtiles, tpw);
       const int per_xcd = (int)cdiv(n_work, 8);
       if (filter) {
@@ -369,7 +374,7 @@ lce_status_t backward_impl(const T* H, const T* W, const T* b, const int64_t* la
                    db ? dbp : (float*)nullptr, lddb, flags, fstride, filter_eps,
                    filter_which == LCE_FILTER_BOTH ? 1 : 0);
       } else {
-        LCE_LAUNCH("k_replay", (k_replay<T, false>), per_xcd * 8, kThreads, gemm_lds_bytes<T>(), s, W, b, Hc,
+        LCE_LAUNCH("k_replay", (k_replay<T, false>), per_xcd * 8, kThreads, (replay_lds_bytes<T, false>()), s, W, b, Hc,
                    yc, mc, lsc, rsc, Cpad, (int)D, (int)V, (int)v0, vtiles, tpw, n_rb, n_work, per_xcd, Gc, ldg,
                    db ? dbp : (float*)nullptr, lddb, (uint8_t*)nullptr, (int64_t)0, 0.f, 0);
       }

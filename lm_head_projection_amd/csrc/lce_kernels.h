@@ -401,11 +401,14 @@ __global__ __launch_bounds__(kThreads) void k_fwd(const T* __restrict__ W, const
 template <typename T> constexpr int gemm_lds_bytes() {
   return sizeof(T) == 2 ? pipe::LDS_BYTES : Geo<T>::LDS_BYTES;
 }
-// The filtered replay adds one vote word per wave after the pipeline's bytes.
-constexpr int kVoteBytes = pipe::NWAVES * 4;
+// The bf16 replay keeps its rows' constants after the pipeline's bytes
+// (16 B per row), and the filtered replay one vote word per wave after them.
+constexpr int kRowStatOffset = pipe::LDS_BYTES, kRowStatBytes = 256 * 16;
+constexpr int kVoteOffset = kRowStatOffset + kRowStatBytes, kVoteBytes = pipe::NWAVES * 4;
 template <typename T, bool FILTER> constexpr int replay_lds_bytes() {
-  return gemm_lds_bytes<T>() + (FILTER ? kVoteBytes : 0);
+  return sizeof(T) == 2 ? kVoteOffset + (FILTER ? kVoteBytes : 0) : gemm_lds_bytes<T>();
 }
+static_assert(kVoteOffset + kVoteBytes <= 160 * 1024, "LDS of one workgroup per CU");
 
 // ============================================================== K3 merge + loss
 // Per supervised row: merge the split partials in split order (online-softmax
@@ -567,7 +570,7 @@ __device__ __forceinline__ void replay_epilogue(f32x16_t (&acc)[Geo<T>::TM][Geo<
                                                 const uint16_t* bias_slice = nullptr,
                                                 uint8_t* __restrict__ flags = nullptr, int64_t fstride = 0,
                                                 float eps = 0.f, uint32_t* votes = nullptr,
-                                                int zero_dead = 0) {
+                                                int zero_dead = 0, const float4* rowstat = nullptr) {
   using C = Cfg<T>;
   using G = Geo<T>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -585,13 +588,17 @@ __device__ __forceinline__ void replay_epilogue(f32x16_t (&acc)[Geo<T>::TM][Geo<
   // pair) and in the db sums; the exponent carries |r_c|.
   uint32_t smask[G::TN];
   float sgn[G::TN];
+  float absr[G::TN];
+  int yrow[G::TN];
 #pragma unroll
   for (int tn = 0; tn < G::TN; ++tn) {
     const int r = n0 + wn * G::WTN + tn * 32 + (lane & 31);
     // p = exp((Z - m) - log s) from the saved statistics (section 04).
-    const float mr = mc[r], lr = lsc[r], rr = rsc[r];
     float sub;  // r_c at the target column
     if constexpr (sizeof(T) == 4) {
+      const float mr = mc[r], lr = lsc[r], rr = rsc[r];
+      yrow[tn] = yc[r];
+      absr[tn] = fabsf(rr);
 #pragma unroll
       for (int tm = 0; tm < G::TM; ++tm)
 #pragma unroll
@@ -601,9 +608,13 @@ __device__ __forceinline__ void replay_epilogue(f32x16_t (&acc)[Geo<T>::TM][Geo<
       smask[tn] = 0u;
       sgn[tn] = 1.f;
     } else {
-      // |r| p = exp2(Z log2e - m log2e - (log s log2e - log2 |r|)); r = 0 gives 0.
+      // |r| p = exp2(Z log2e - m log2e - (log s log2e - log2 |r|)); r = 0 gives
+      // 0.  The row's constants come from LDS (written once per workgroup).
+      const float4 st = rowstat[wn * G::WTN + tn * 32 + (lane & 31)];
+      const float ml = st.x, ll = st.y, rr = st.z;
       const float ar = fabsf(rr);
-      const float ml = mr * kLog2e, ll = lr * kLog2e - log2f(ar);
+      yrow[tn] = __float_as_int(st.w);
+      absr[tn] = ar;
 #pragma unroll
       for (int tm = 0; tm < G::TM; ++tm)
 #pragma unroll
@@ -614,7 +625,7 @@ __device__ __forceinline__ void replay_epilogue(f32x16_t (&acc)[Geo<T>::TM][Geo<
       smask[tn] = neg ? 0x80008000u : 0u;
       sgn[tn] = neg ? -1.f : 1.f;
     }
-    const int d = yc[r] - vbase;
+    const int d = yrow[tn] - vbase;
     if ((unsigned)d < (unsigned)G::WTM) {
 #pragma unroll
       for (int tm = 0; tm < G::TM; ++tm)
@@ -647,10 +658,8 @@ __device__ __forceinline__ void replay_epilogue(f32x16_t (&acc)[Geo<T>::TM][Geo<
     int dd[G::TN];
 #pragma unroll
     for (int tn = 0; tn < G::TN; ++tn) {
-      const int r = n0 + wn * G::WTN + tn * 32 + (lane & 31);
-      const float ar = fabsf(rsc[r]);
-      thr[tn] = ar > 0.f ? eps * ar : INFINITY;
-      dd[tn] = yc[r] - vbase;
+      thr[tn] = absr[tn] > 0.f ? eps * absr[tn] : INFINITY;
+      dd[tn] = yrow[tn] - vbase;
     }
     uint32_t mine = 0;
 #pragma unroll
@@ -682,9 +691,9 @@ __device__ __forceinline__ void replay_epilogue(f32x16_t (&acc)[Geo<T>::TM][Geo<
     // leaves lane l with entries 0..15 and lane l+32 with 16..31, each
     // written as 32 contiguous bytes.
     const int h = lane >> 5;
-    T* gb = Gc + ((int64_t)(n0 / pipe::GB_ROWS) * (ldg / pipe::GB_COLS) + (vbase - v0) / pipe::GB_COLS) *
-                     pipe::GB_ELEMS +
-            (wn * G::WTN + (lane & 31)) * pipe::GB_COLS + 16 * h;
+    const int64_t tile = ((int64_t)(n0 / pipe::GB_ROWS) * (ldg / pipe::GB_COLS) + (vbase - v0) / pipe::GB_COLS) *
+                         pipe::GB_ELEMS;
+    T* gb = Gc + tile + (wn * G::WTN + (lane & 31)) * pipe::GB_COLS + 16 * h;
 #pragma unroll
     for (int tn = 0; tn < G::TN; ++tn)
 #pragma unroll
@@ -708,6 +717,7 @@ __device__ __forceinline__ void replay_epilogue(f32x16_t (&acc)[Geo<T>::TM][Geo<
         *reinterpret_cast<u32x4*>(dst) = u32x4{d[0], d[1], d[4], d[5]};
         *reinterpret_cast<u32x4*>(dst + 8) = u32x4{d[2], d[3], d[6], d[7]};
       }
+
   } else {
     // Store G row-major (4 consecutive vocabulary entries of one row per lane and group).
 #pragma unroll
@@ -783,9 +793,22 @@ __global__ __launch_bounds__(kThreads) void k_replay(
   const int nsteps = sizeof(T) == 2 ? (D + pipe::BK - 1) / pipe::BK : (D + C::BK - 1) / C::BK;
   if constexpr (sizeof(T) == 2) {
     float* red = reinterpret_cast<float*>(smem_raw + pipe::RING_BYTES);
+    // The workgroup's 256 rows are the same for every tile: their exponent
+    // constants (m log2e, log s log2e - log2 |r|), r and label go to LDS once.
+    // Loading them in each epilogue would wait on the in-order vector-memory
+    // counter behind the next stage's loads.
+    float4* rowstat = reinterpret_cast<float4*>(smem_raw + kRowStatOffset);
+    if (threadIdx.x < C::BN) {
+      const int r = n0 + threadIdx.x;
+      const float rr = rsc[r];
+      rowstat[threadIdx.x] = float4{mc[r] * kLog2e, lsc[r] * kLog2e - log2f(fabsf(rr)), rr,
+                                    __int_as_float(yc[r])};
+    }
+    pipe::wait_lgkm0();  // published by the pipeline's first barrier
     f32x16_t acc[G::TM][G::TN];
     // Each wave's epilogue ends with TN*TM*2 G-tile stores (plus, with a
-    // bias, the db stores of some waves).
+    // bias, the db stores of some waves and, with the filter, the flag stores
+    // of some).
     pipe::run<0, true, G::TN * G::TM * 2>(
         ntiles, nsteps, D, smem_raw, acc,
         [&](int t, pipe::Opnd& A, pipe::Opnd& B, int& k0) {
@@ -796,7 +819,7 @@ __global__ __launch_bounds__(kThreads) void k_replay(
         [&](int t, f32x16_t (&acc)[G::TM][G::TN]) {
           replay_epilogue<T, FILTER>(acc, bias, v0 + (vt0 + t) * C::BM, n0, V, v0, yc, mc, lsc, rsc, Gc, ldg, dbp,
                                      lddb, rb, red, true, pipe::bias_slice(smem_raw, t), flags, fstride, eps,
-                                     reinterpret_cast<uint32_t*>(smem_raw + pipe::LDS_BYTES), zero_dead);
+                                     reinterpret_cast<uint32_t*>(smem_raw + kVoteOffset), zero_dead, rowstat);
         },
         true, reinterpret_cast<const uint16_t*>(bias), V);
   } else {
