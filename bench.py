@@ -201,7 +201,7 @@ def main():
         dH_parts = [torch.empty_like(H) for _ in range(P)]
         g1 = grad if args.reduction == "none" else grad.reshape(1)
 
-        def step():
+        def step(mark=None):
             st, C = _lib.lce_compact_valid(labels, mask, V, wl.ignore_index, idx, ws, stream)
             assert st == _lib.LCE_OK, _lib.status_string(st)
             for p in range(P):
@@ -212,6 +212,8 @@ def main():
             pc = parts[: P * 3 * C].view(P, 3 * C)
             st = _lib.lce_merge_shards(pc, bounds, labels, idx, C, red, weights, num, loss, m, logs, ws, stream)
             assert st == _lib.LCE_OK, _lib.status_string(st)
+            if mark is not None:
+                mark()
             for p in range(P):
                 v0, v1 = bounds[p], bounds[p + 1]
                 st = _lib.lce_backward_shard(H, W[v0:v1], None if b is None else b[v0:v1], labels, idx, C, v0, red,
@@ -220,7 +222,7 @@ def main():
                 assert st == _lib.LCE_OK, _lib.status_string(st)
             return C
 
-    def step_single():
+    def step_single(mark=None):
         st, C = _lib.lce_compact_valid(labels, mask, V, wl.ignore_index, idx, ws, stream)
         assert st == _lib.LCE_OK, _lib.status_string(st)
         if plain and train:
@@ -231,6 +233,8 @@ def main():
         assert st == _lib.LCE_OK, _lib.status_string(st)
         if not train:
             return C
+        if mark is not None:
+            mark()
         if args.filter_eps is not None:
             st = _lib.lce_backward_filtered(H, W, b, labels, idx, C, red, weights, num, m, logs, grad,
                                             args.filter_eps, dH, dW, db, ws, stream,
@@ -278,6 +282,23 @@ def main():
     torch.cuda.synchronize()
     kern = _lib.profile_stop()
     log(f"[bench] per-kernel pass done ({sum(v[0] for v in kern.values()) / args.steps:.3f} ms/step in kernels)")
+
+    # Forward (compaction included) and backward apart: the same K steps once
+    # more, with one more event between the two on the stream.
+    phases = None
+    if train:
+        marks = []
+        for _ in range(args.steps):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record(stream)
+            step(mark=lambda e=e: e[1].record(stream))
+            e[2].record(stream)
+            marks.append(e)
+        torch.cuda.synchronize()
+        fwd = sum(e[0].elapsed_time(e[1]) for e in marks) / args.steps
+        bwd = sum(e[1].elapsed_time(e[2]) for e in marks) / args.steps
+        phases = {"forward_ms": fwd, "backward_ms": bwd}
+        log(f"[bench] phases: forward {fwd:.3f} ms, backward {bwd:.3f} ms per step")
 
     flops_step = (8.0 if train else 2.0) * C * D * V
     tflops = flops_step / (ms * 1e-3) / 1e12
@@ -331,6 +352,7 @@ def main():
         "pct_peak": 100.0 * tflops / peak,
         "positions_per_s": N * args.steps / (total_ms * 1e-3),
         "flops_per_step": flops_step,
+        "phases": phases,
         "peak_extra_mem_bytes": int(peak_extra),
         "workspace_bytes": int(ws.numel()),
         "dense_logits_bytes_avoided": int(N) * int(V) * (2 if wl.dtype == torch.bfloat16 else 4),

@@ -909,13 +909,16 @@ __device__ __forceinline__ void grad_store(const f32x16_t (&acc)[Geo<T>::TM][Geo
         const int r = m0 + wm * G::WTM + acc_row(tm, i, lane);
         const float a = acc[tm][tn][i];
         if (dh) {
+          // A slot element has one owner per launch and launches run in
+          // chunk order, so the L2 atomic add (no return) sums exactly what a
+          // load-add-store would, without the wave waiting for the load.
           float* p = slot + (int64_t)r * D + n;
-          *p = accumulate ? (*p + a) : a;
+          if (accumulate) (void)__hip_atomic_fetch_add(p, a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          else *p = a;
         } else if (r < vc) {
           dW[(int64_t)(v0 + r) * D + n] = from_f32<T>(a);
         }
       }
-      // One 32x32 block at a time keeps the read-modify-write registers bounded.
       __builtin_amdgcn_sched_barrier(0);
     }
   }
