@@ -304,6 +304,8 @@ def main():
     tflops = flops_step / (ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if wl.dtype == torch.bfloat16 else PEAK_FP32_TFLOPS
     kf = kernel_flops(C, D, V, args.mode)
+    if args.filter_eps is not None:
+        kf.pop("k_grad")  # the filter skips a data-dependent part of its products
     kernels = {}
     for name, (tot, n) in sorted(kern.items(), key=lambda kv: -kv[1][0]):
         e = {"total_ms_per_step": tot / args.steps, "launches_per_step": n / args.steps,
@@ -331,7 +333,9 @@ def main():
     out = {
         "metric": METRIC if train else METRIC_FWD,
         "note": (f"{args.shards} vocabulary shards run one after another; the dH sum over shards (an "
-                 "all-reduce across devices) is not part of the step") if args.mode == "shard" else None,
+                 "all-reduce across devices) is not part of the step") if args.mode == "shard" else
+                ("gradient filter on: tflops counts the dense 8*C*D*V (a dense-equivalent rate); k_grad skips "
+                 "the products of dropped blocks") if args.filter_eps is not None else None,
         "value": C * args.steps / (total_ms * 1e-3),
         "unit": "supervised tokens/s",
         "n_gpus": 1,
