@@ -36,6 +36,13 @@ template <> __device__ __forceinline__ uint16_t from_f32<uint16_t>(float x) {
   // Round to nearest even (hardware conversion on gfx950).
   return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// Two floats to a bf16 pair (a in the low half), round to nearest even: one
+// v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
 
 // ---------------------------------------------------------------- tile config
 template <typename T> struct Cfg;

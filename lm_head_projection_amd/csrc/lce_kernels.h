@@ -702,10 +702,7 @@ __device__ __forceinline__ void replay_epilogue(f32x16_t (&acc)[Geo<T>::TM][Geo<
         const uint32_t km = ((keep >> tm) & 1u) ? ~0u : 0u;
 #pragma unroll
         for (int k = 0; k < 8; ++k)
-          d[k] = (((uint32_t)from_f32<uint16_t>(acc[tm][tn][2 * k]) |
-                   ((uint32_t)from_f32<uint16_t>(acc[tm][tn][2 * k + 1]) << 16)) ^
-                  smask[tn]) &
-                 km;
+          d[k] = (pack_bf16x2(acc[tm][tn][2 * k], acc[tm][tn][2 * k + 1]) ^ smask[tn]) & km;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           // lanes 32..63 of d[k] <-> lanes 0..31 of d[k + 4]
@@ -1058,8 +1055,10 @@ __global__ void k_dh_finalize(const float* __restrict__ slots, int S, int64_t sl
         o[3] += v[3];
       }
     }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) dH[n * D + d + j] = from_f32<T>(o[j]);
+    if constexpr (sizeof(T) == 2)
+      *reinterpret_cast<uint2*>(dH + n * D + d) = uint2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+    else
+      *reinterpret_cast<f32x4_t*>(dH + n * D + d) = f32x4_t{o[0], o[1], o[2], o[3]};
   }
 }
 
