@@ -203,3 +203,33 @@ def test_fullsize_packed_filter_keeps_target_blocks():
     dh, _, _ = O.filtered_rows_grad(Hd, Wd, bd, y, f.m, f.logs, 10.0, rows, [], 1.0)
     t = tol(wl.dtype)
     assert_grad_close("dH rows filtered", dH[rows], dh, t["grad"])
+
+
+def test_fullsize_packed_memory_far_below_dense_logits():
+    """A forward + backward through the autograd wrapper at the packed sizes:
+    the device memory it adds beyond the inputs and the gradient buffers
+    (workspace, index and statistics arrays) stays under a quarter of the
+    dense bf16 N x V logits, and no block the allocator holds afterwards is
+    as large as those logits."""
+    from lm_head_projection_amd import linear_cross_entropy
+    wl, _, _ = workload("packed")
+    dev = "cuda:0"
+    H = wl.H.to(dev).requires_grad_(True)
+    W = wl.W.to(dev).requires_grad_(True)
+    labels = wl.labels.to(dev)
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    loss = linear_cross_entropy(H, W, labels)
+    loss.backward()
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated() - base
+    grads = (H.numel() + W.numel()) * H.element_size()
+    dense = wl.N * wl.V * 2
+    say(f"[fullsize] packed: peak extra {peak / 1e9:.2f} GB (gradients {grads / 1e9:.2f} GB), "
+        f"dense logits {dense / 1e9:.2f} GB")
+    assert torch.isfinite(loss)
+    assert peak - grads < dense / 4
+    for seg in torch.cuda.memory_snapshot():
+        for blk in seg["blocks"]:
+            assert blk["size"] < dense, blk
