@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
+#include <set>
 #include <cstdint>
 #include <cstring>
 #include <string>
@@ -157,8 +159,15 @@ bool make_layout(int64_t N, int64_t D, int64_t V, lce_dtype_t dt, Layout& L) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Once per (device, kernel): each kernel always asks for the same LDS size,
+// and the attribute call costs host time that the GPU would wait for.
 template <typename T> void set_lds_attr(const void* fn, int bytes) {
-  (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  static std::mutex mu;
+  static std::set<std::pair<int, const void*>> done;
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (done.insert({dev, fn}).second) (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
 
 // Number of vocabulary splits for the forward grid: minimise
