@@ -122,7 +122,8 @@ lce_status_t lce_forward(const void* H, const void* W, const void* b, const int6
  *   rows of dH for unsupervised positions are exactly 0.
  *   db [V] device, type dt, or NULL (skip the bias gradient).
  * Deterministic: the same inputs give bitwise-identical outputs (ordered
- * reductions, no floating-point atomics).
+ * reductions; the only floating-point atomics add into partial sums that
+ * have one writer per kernel launch, with launches in a fixed order).
  * C == 0: dH, dW and db are zero-filled, returns LCE_OK_EMPTY. */
 lce_status_t lce_backward(const void* H, const void* W, const void* b, const int64_t* labels,
                           const int32_t* valid_idx, int64_t C, int64_t N, int64_t D, int64_t V,
