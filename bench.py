@@ -144,8 +144,8 @@ def cpu_baseline(wl, target_s: float, forward_only: bool = False):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
-              "multi-GPU sharding is a design note, not part of this build.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the library has no "
+              "multi-GPU path; how it would shard is described in the design notes.", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
