@@ -238,3 +238,35 @@ def test_host_argument_errors():
     Hodd = torch.zeros(N, 6, device=dev)
     Wodd = torch.zeros(V, 6, device=dev)
     assert _lib.lce_forward(Hodd, Wodd, None, labels, idx, C, loss, m, logs, None, ws) == _lib.LCE_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_no_positions_at_all(dtype):
+    """N = 0 (an empty batch, not only C = 0): the loss is exactly 0 and the
+    gradients are exactly 0 (dH is empty), through the autograd wrapper."""
+    from lm_head_projection_amd import linear_cross_entropy
+    dev = "cuda:0"
+    g = torch.Generator().manual_seed(5)
+    H = torch.zeros(0, 64, dtype=dtype, device=dev, requires_grad=True)
+    W = (0.02 * torch.randn(300, 64, generator=g)).to(dtype).to(dev).requires_grad_(True)
+    b = (0.01 * torch.randn(300, generator=g)).to(dtype).to(dev).requires_grad_(True)
+    labels = torch.zeros(0, dtype=torch.int64, device=dev)
+    loss = linear_cross_entropy(H, W, labels, bias=b)
+    loss.backward()
+    torch.cuda.synchronize()
+    assert loss.item() == 0.0
+    assert H.grad.shape == (0, 64)
+    assert torch.count_nonzero(W.grad).item() == 0 and torch.count_nonzero(b.grad).item() == 0
+
+
+def test_unsupported_shape_is_refused():
+    """bf16 rows must be whole 16-byte vectors (D a multiple of 8): D = 12 is
+    refused with LCE_ERR_UNSUPPORTED before any kernel runs."""
+    from lm_head_projection_amd import linear_cross_entropy
+    dev = "cuda:0"
+    H = torch.randn(16, 12, device=dev).to(torch.bfloat16)
+    W = torch.randn(40, 12, device=dev).to(torch.bfloat16)
+    labels = torch.randint(0, 40, (16,), device=dev)
+    with pytest.raises(_lib.LCEError) as e:
+        linear_cross_entropy(H, W, labels)
+    assert e.value.status == _lib.LCE_ERR_UNSUPPORTED
