@@ -25,9 +25,10 @@
  *    with fp32 accumulation, the scores Z and every statistic are fp32.
  *  - D must be a multiple of 8 (bf16) or 4 (fp32).
  *  - The caller owns all memory, including the workspace (size it with
- *    lce_workspace_size).  The library never allocates device memory and keeps
- *    no state between calls (apart from the optional profiling switch at the
- *    end of this header).  Inputs are never written.
+ *    lce_workspace_size).  The library never allocates device memory.  Its
+ *    only state between calls is a per-device record of the kernel
+ *    attributes it has set and the optional profiling switch at the end of
+ *    this header.  Inputs are never written.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream).
  *    Only lce_compact_valid synchronises the stream (to return C).
  *  - No exception crosses the ABI; every call returns an lce_status_t.
