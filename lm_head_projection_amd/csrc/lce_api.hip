@@ -233,9 +233,8 @@ int choose_dh_splits(int64_t kpad, int64_t Cpad, int64_t Npad, int64_t n_dh_tile
   return best;
 }
 
-// Vocabulary tiles per replay workgroup: minimise (waves of workgroups) x
-// (tiles per workgroup) with at most 8 tiles, ties to fewer tiles.
-// Replay tiles per workgroup: minimises the makespan in pipeline stages,
+// Replay tiles per workgroup (at most 8, ties to fewer): minimises the
+// makespan in pipeline stages,
 // waves * (tpw * nsteps + kItemStages), where kItemStages stands for the
 // per-workgroup cost the tile walk cannot hide (the first stages' load
 // latency and the last tile's epilogue).

@@ -44,8 +44,8 @@ __device__ __forceinline__ const uint16_t* bias_slice(const char* lds, int t) {
   return reinterpret_cast<const uint16_t*>(lds + BIAS_OFFSET + (t & (BIAS_SLOTS - 1)) * BIAS_SLOT_BYTES);
 }
 constexpr int WGM = 2, WGN = NWAVES / 2, WTM = BM / WGM, WTN = BN / WGN, TM = WTM / 32, TN = WTN / 32;
-constexpr int DMA_PER_OPND = OPND_BYTES / 1024 / NWAVES;  // 1 KB DMA instructions per wave: 8
-constexpr int DMA_PER_STAGE = 2 * DMA_PER_OPND;           // 16 per wave per stage
+constexpr int DMA_PER_OPND = OPND_BYTES / 1024 / NWAVES;  // 1 KB DMA instructions per wave and operand: 4
+constexpr int DMA_PER_STAGE = 2 * DMA_PER_OPND;           // 8 per wave per stage
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
