@@ -270,3 +270,27 @@ def test_unsupported_shape_is_refused():
     with pytest.raises(_lib.LCEError) as e:
         linear_cross_entropy(H, W, labels)
     assert e.value.status == _lib.LCE_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_many_positions_narrow_chunks(dtype):
+    """N = 40000 positions: the padded rows (40192) cap one chunk of the
+    gradient tile store at 2 GB of 32-bit buffer offsets, so the backward
+    runs in chunks of 26624 (bf16) or 13312 (fp32) vocabulary entries, a
+    width that is no power of two, with a ragged last chunk.  64 supervised
+    rows keep the oracle cheap; every output element is checked."""
+    wl = WL.make_random(40000, 256, 60000, dtype=dtype, seed=31, ignore_frac=0.1)
+    sub = WL.supervised_subset(wl, 64)
+    say(f"[parity] N=40000 D=256 V=60000 {dtype}: 64 supervised rows")
+    r = run_gpu(sub)
+    Hd, Wd = sub.H.double().numpy(), sub.W.double().numpy()
+    bd = sub.b.double().numpy()
+    f, g = O.dense_forward_backward(Hd, Wd, bd, sub.labels.numpy(), sub.mask.numpy(), 1.0)
+    t = tol(dtype)
+    assert r.C == f.C == 64
+    assert abs(r.loss - f.loss) <= t["loss"] * abs(f.loss)
+    assert_stat_close("m", r.m[f.idx], f.m[f.idx], t["stat"])
+    assert_stat_close("logs", r.logs[f.idx], f.logs[f.idx], t["stat"])
+    assert_grad_close("dH", r.dH, g.dH, t["grad"])
+    assert_grad_close("dW", r.dW, g.dW, t["grad"])
+    assert_grad_close("db", r.db, g.db, t["grad"])
