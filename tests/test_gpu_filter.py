@@ -220,3 +220,29 @@ def test_autograd_filter_eps_matches_the_entry_point():
     np.testing.assert_array_equal(to_np(H.grad), dH0)
     np.testing.assert_array_equal(to_np(W.grad), dW0)
     np.testing.assert_array_equal(to_np(b.grad), db0)
+
+
+def test_filter_stage_list_overflow_falls_back_exactly():
+    """115000 supervised rows: a dW item's live stage list (one entry per 32
+    rows) would overflow its LDS capacity, so the kernel runs the full range,
+    where dead blocks of G are stored as zeros.  Labels lie in [0, 64) and
+    eps = 10, so only the first two column blocks are live: dW rows from 64
+    on are exactly 0, and sampled dW and dH rows match the oracle."""
+    wl = WL.make_random(115000, 128, 1024, dtype=torch.bfloat16, seed=41, ignore_frac=0.0, bias=False,
+                        w_scale=0.02)
+    g = torch.Generator().manual_seed(42)
+    wl.labels = torch.randint(0, 64, (wl.N,), generator=g)
+    say("[filter] 115000 rows, eps 10: GPU")
+    st, dH, dW, db = run_filtered(wl, 10.0)
+    assert st == _lib.LCE_OK
+    assert np.all(dW[64:] == 0.0)
+    say("[filter] 115000 rows: oracle statistics and sampled rows")
+    Hd, Wd, y = wl.H.double().numpy(), wl.W.double().numpy(), wl.labels.numpy()
+    f = O.dense_forward(Hd, Wd, None, y)
+    rng = np.random.default_rng(43)
+    rows = np.sort(rng.choice(f.idx, 4, replace=False))
+    cols = np.array([0, 17, 40, 63])
+    dh, dw, _ = O.filtered_rows_grad(Hd, Wd, None, y, f.m, f.logs, 10.0, rows, cols, 1.0)
+    t = tol(wl.dtype)
+    assert_grad_close("dH rows", dH[rows], dh, t["grad"])
+    assert_grad_close("dW rows", dW[cols], dw, t["grad"])
