@@ -81,6 +81,22 @@ def kernel_flops(C, D, V, mode="train"):
     return {"k_fwd": 2.0 * C * D * V, "k_replay": 2.0 * C * D * V, "k_grad": 4.0 * C * D * V}
 
 
+def kernel_bytes(C, N, D, V, esz, has_mask, has_bias):
+    """Algorithmic HBM bytes per launch of the memory-bound kernels: the
+    compaction (labels and mask read, indices written), the row gather, and
+    the two finalisations.  k_dh_finalize reads at least one fp32 partial per
+    supervised element (more when the library splits dH over several slots),
+    so its figure is a lower bound."""
+    cpad = -(-C // 256) * 256
+    per_pos = 8 + (1 if has_mask else 0)
+    out = {"k_cmp_count": N * per_pos, "k_cmp_scatter": N * per_pos + 4 * C,
+           "k_gather": C * D * esz + cpad * D * esz,
+           "k_dh_finalize": C * D * 4 + N * D * esz}
+    if has_bias:
+        out["k_db_finalize"] = (cpad // 256) * (-(-V // 256) * 256) * 4 + V * esz
+    return out
+
+
 def stored_traffic(kernel: str, workload: str):
     """HBM bytes per launch of `kernel` on `workload`, from the committed
     counter profile profiles/<kernel>_<workload>_hbm_traffic.md, or None when
@@ -306,12 +322,17 @@ def main():
     kf = kernel_flops(C, D, V, args.mode)
     if args.filter_eps is not None:
         kf.pop("k_grad")  # the filter skips a data-dependent part of its products
+    kb = kernel_bytes(C, N, D, V, 2 if wl.dtype == torch.bfloat16 else 4, mask is not None, b is not None)
     kernels = {}
     for name, (tot, n) in sorted(kern.items(), key=lambda kv: -kv[1][0]):
         e = {"total_ms_per_step": tot / args.steps, "launches_per_step": n / args.steps,
              "avg_ms": tot / max(n, 1)}
         if name in kf:
             e["tflops"] = kf[name] * args.steps / (tot * 1e-3) / 1e12
+        if name in kb:
+            e["hbm_gbps"] = kb[name] / (e["avg_ms"] * 1e-3) / 1e9
+            if name == "k_dh_finalize":
+                e["hbm_gbps_lower_bound"] = True
         kernels[name] = e
     dom = max((k for k in kernels if k in kf), key=lambda k: kernels[k]["total_ms_per_step"])
     tr = stored_traffic(dom, args.workload)

@@ -1068,6 +1068,9 @@ __global__ void k_db_finalize(const float* __restrict__ dbp, int n_rb, int64_t l
                               T* __restrict__ db) {
   for (int v = blockIdx.x * blockDim.x + threadIdx.x; v < V; v += gridDim.x * blockDim.x) {
     float s = 0.f;
+    // Unrolled so that several row blocks' loads are in flight at once; the
+    // sum keeps the ascending row-block order.
+#pragma unroll 8
     for (int rb = 0; rb < n_rb; ++rb) s += dbp[(int64_t)rb * lddb + v];
     db[v] = from_f32<T>(s);
   }
