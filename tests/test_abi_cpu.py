@@ -126,3 +126,17 @@ def test_python_binding_names_match_c_abi():
               "lce_backward_ex", "lce_backward_filtered", "lce_forward_shard", "lce_merge_shards",
               "lce_backward_shard"):
         assert callable(getattr(_lib, n))
+
+
+def test_wrapper_rejects_unknown_options_before_any_library_call():
+    """The autograd wrapper refuses an unknown filter choice or reduction
+    before it allocates or calls into the library (CPU tensors suffice)."""
+    import torch
+    from lm_head_projection_amd import linear_cross_entropy
+    H = torch.zeros(4, 8)
+    W = torch.zeros(5, 8)
+    y = torch.zeros(4, dtype=torch.int64)
+    with pytest.raises(ValueError):
+        linear_cross_entropy(H, W, y, filter_eps=0.1, filter_grads="dw")
+    with pytest.raises(KeyError):
+        linear_cross_entropy(H, W, y, reduction="median")
