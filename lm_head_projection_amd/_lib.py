@@ -10,9 +10,8 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-# LCE_LIBRARY may name another build of the same library (e.g. to compare two
-# builds in one process); by default the in-tree build is used.
-LIB_PATH = os.environ.get("LCE_LIBRARY") or os.path.join(PKG, "liblce.so")
+# The in-tree build (lm_head_projection_amd/build.py); no other library is loaded.
+LIB_PATH = os.path.join(PKG, "liblce.so")
 
 LCE_DTYPE_F32 = 0
 LCE_DTYPE_BF16 = 1
@@ -35,6 +34,7 @@ REDUCTIONS = {"mean": LCE_REDUCTION_MEAN, "sum": LCE_REDUCTION_SUM, "none": LCE_
 # Every entry point that include/lce.h declares.
 EXPORTS = (
     "lce_workspace_size",
+    "lce_forward_workspace_size",
     "lce_compact_valid",
     "lce_forward",
     "lce_backward",
@@ -71,6 +71,8 @@ def load() -> ctypes.CDLL:
     vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
     lib.lce_workspace_size.argtypes = [i64, i64, i64, ctypes.c_int]
     lib.lce_workspace_size.restype = sz
+    lib.lce_forward_workspace_size.argtypes = [i64, i64, i64, ctypes.c_int]
+    lib.lce_forward_workspace_size.restype = sz
     lib.lce_compact_valid.argtypes = [vp, vp, i64, i64, i64, vp, ctypes.POINTER(i64), vp, sz, vp]
     lib.lce_compact_valid.restype = ctypes.c_int
     lib.lce_forward.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
@@ -138,6 +140,10 @@ def dtype_code(dtype) -> int:
 
 def lce_workspace_size(N: int, D: int, V: int, dtype) -> int:
     return int(load().lce_workspace_size(N, D, V, dtype_code(dtype)))
+
+
+def lce_forward_workspace_size(N: int, D: int, V: int, dtype) -> int:
+    return int(load().lce_forward_workspace_size(N, D, V, dtype_code(dtype)))
 
 
 def lce_compact_valid(labels, mask, V: int, ignore_index: int, valid_idx, ws, stream=None):
