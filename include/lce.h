@@ -25,7 +25,8 @@
  *    with fp32 accumulation, the scores Z and every statistic are fp32.
  *  - D must be a multiple of 8 (bf16) or 4 (fp32).
  *  - The caller owns all memory, including the workspace (size it with
- *    lce_workspace_size).  The library never allocates device memory.  Its
+ *    lce_workspace_size, or lce_forward_workspace_size for the compaction
+ *    and forward calls alone).  The library never allocates device memory.  Its
  *    only state between calls is a per-device record of the kernel
  *    attributes it has set and the optional profiling switch at the end of
  *    this header.  Inputs are never written.
@@ -56,7 +57,7 @@ typedef enum {
                               should skip the optimizer step) */
   LCE_ERR_ARG = -1,        /* null or inconsistent argument, misaligned pointer */
   LCE_ERR_LABEL = -2,      /* a supervised label lies outside [0, V) */
-  LCE_ERR_WORKSPACE = -3,  /* ws_bytes below lce_workspace_size(...) */
+  LCE_ERR_WORKSPACE = -3,  /* ws_bytes below the size the call needs */
   LCE_ERR_HIP = -4,        /* a HIP runtime call or kernel launch failed */
   LCE_ERR_UNSUPPORTED = -5 /* shape outside the documented limits */
 } lce_status_t;
@@ -81,6 +82,17 @@ typedef enum {
  * vocabulary chunk of the softmax-gradient tile store (N x min(V, 32768)) and
  * the fp32 dH accumulators (at most 4 x N x D).  Returns 0 for invalid sizes. */
 size_t lce_workspace_size(int64_t N, int64_t D, int64_t V, lce_dtype_t dt);
+
+/* Bytes of device workspace that the compaction and forward calls alone need
+ * (lce_compact_valid, lce_forward, lce_forward_ex, lce_forward_shard with the
+ * shard's V): the gathered supervised rows and the per-split row partials,
+ * about N x D elements plus 0.5 KB per position.  A caller can free this
+ * buffer after the forward call and allocate the lce_workspace_size buffer
+ * only for the backward call, so that nothing beyond m and logs (the two
+ * N-vectors that section 02 of the glenzli.com page saves) is held between
+ * the passes.  Returns 0 for invalid sizes; never more than
+ * lce_workspace_size. */
+size_t lce_forward_workspace_size(int64_t N, int64_t D, int64_t V, lce_dtype_t dt);
 
 /* Valid-token compaction (section 01 definition of a_i and C; the
  * ChunkedLinearCrossEntropy page's prompt filtering).

@@ -24,10 +24,7 @@ using namespace lce;
 
 namespace {
 
-#ifndef LCE_VOCAB_CHUNK
-#define LCE_VOCAB_CHUNK 32768
-#endif
-constexpr int64_t kVcMax = LCE_VOCAB_CHUNK;  // vocabulary chunk of the gradient tile store
+constexpr int64_t kVcMax = 32768;    // vocabulary chunk of the gradient tile store
 constexpr int kMaxSplit = 64;         // vocabulary splits of the forward pass
 constexpr int kDhSlotRows = 4;        // the dH slots hold 4 x Npad rows of D fp32 values
 constexpr int kMaxDhSlots = 16;       // k-splits of the dH GEMM (at most)
@@ -106,7 +103,8 @@ struct Layout {
   size_t pm, ps, tgt, lrow;
   // backward
   size_t mc, lsc, rsc, inv, G, slots, dbp, flags;
-  size_t total;
+  size_t fwd_total;  // compaction + forward calls
+  size_t total;      // every call (the backward region is the larger one)
   int64_t Npad, Vpad, Vc, nblk;
 };
 
@@ -143,6 +141,7 @@ bool make_layout(int64_t N, int64_t D, int64_t V, lce_dtype_t dt, Layout& L) {
   L.tgt = take(L.Npad * 4);
   L.lrow = take(L.Npad * 4);
   const size_t fwd_end = off;
+  L.fwd_total = fwd_end;
   // backward region overlays the forward region (the calls never overlap)
   off = common_end;
   L.mc = take(L.Npad * 4);
@@ -365,7 +364,10 @@ lce_status_t backward_impl(const T* H, const T* W, const T* b, const int64_t* la
   set_lds_attr<T>((const void*)k_replay<T, true>, replay_lds_bytes<T, true>());
   set_lds_attr<T>((const void*)k_grad<T>, grad_lds_bytes<T>());
 
-  int S = 0;  // dH k-splits, fixed by the first (widest) chunk
+  // dH slots: chunk 0 (the widest) fixes their number S and stores every one
+  // of them; later chunks, whose splits never outnumber S, add into theirs.
+  // k_dh_finalize sums exactly these S slots.
+  int S = 0;
   for (int64_t v0 = 0, chunk = 0; v0 < V; v0 += L.Vc, ++chunk) {
     const int vc = (int)std::min<int64_t>(L.Vc, V - v0);
     const int vtiles = (int)cdiv(vc, Cf::BM);
@@ -391,7 +393,8 @@ lce_status_t backward_impl(const T* H, const T* W, const T* b, const int64_t* la
     if (chunk == 0)
       S = choose_dh_splits(kpad, Cpad, L.Npad, (int64_t)n_dh_mt * n_nt, (int64_t)vtiles * n_nt, Cf::BK);
     int64_t ks_len = rup(cdiv(kpad, S), Cf::BK);
-    const int S_eff = (int)cdiv(kpad, ks_len);
+    const int S_eff = (int)cdiv(kpad, ks_len);  // non-empty splits; a later chunk has ks_len >= kpad / S, so S_eff <= S
+    if (chunk == 0) S = S_eff;
     const int n_dh = n_dh_mt * n_nt * S_eff;
     const int n_dw = vtiles * n_nt;
     const int per_xcd = (int)(cdiv(n_dh, 8) + cdiv(n_dw, 8));
@@ -465,7 +468,7 @@ lce_status_t forward_entry(const void* H, const void* W, const void* b, const in
     LCE_TRY(shape_supported(N, D, V, dt));
     Layout L;
     if (!make_layout(N, D, V, dt, L)) return LCE_ERR_ARG;
-    if (ws_bytes < L.total) return LCE_ERR_WORKSPACE;
+    if (ws_bytes < L.fwd_total) return LCE_ERR_WORKSPACE;
     char* w = static_cast<char*>(ws);
     if (dt == LCE_DTYPE_BF16)
       return forward_impl<uint16_t>((const uint16_t*)H, (const uint16_t*)W, (const uint16_t*)b, labels,
@@ -527,6 +530,12 @@ size_t lce_workspace_size(int64_t N, int64_t D, int64_t V, lce_dtype_t dt) {
   Layout L;
   if (!make_layout(N, D, V, dt, L)) return 0;
   return L.total;
+}
+
+size_t lce_forward_workspace_size(int64_t N, int64_t D, int64_t V, lce_dtype_t dt) {
+  Layout L;
+  if (!make_layout(N, D, V, dt, L)) return 0;
+  return L.fwd_total;
 }
 
 const char* lce_status_string(lce_status_t st) {

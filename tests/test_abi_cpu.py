@@ -122,7 +122,7 @@ def test_host_argument_checks_return_before_any_hip_call(lib):
 
 
 def test_python_binding_names_match_c_abi():
-    for n in ("lce_workspace_size", "lce_compact_valid", "lce_forward", "lce_backward", "lce_forward_ex",
+    for n in ("lce_workspace_size", "lce_forward_workspace_size", "lce_compact_valid", "lce_forward", "lce_backward", "lce_forward_ex",
               "lce_backward_ex", "lce_backward_filtered", "lce_forward_shard", "lce_merge_shards",
               "lce_backward_shard"):
         assert callable(getattr(_lib, n))
@@ -138,5 +138,67 @@ def test_wrapper_rejects_unknown_options_before_any_library_call():
     y = torch.zeros(4, dtype=torch.int64)
     with pytest.raises(ValueError):
         linear_cross_entropy(H, W, y, filter_eps=0.1, filter_grads="dw")
-    with pytest.raises(KeyError):
+    with pytest.raises(ValueError):
         linear_cross_entropy(H, W, y, reduction="median")
+
+
+def test_wrapper_checks_shapes_counts_and_device_before_any_library_call(monkeypatch):
+    """Every inconsistent argument is refused in Python, before an allocation
+    or a call into the library: a wrong D, element counts of labels, mask,
+    loss_weights and bias that differ from N or V, mixed dtypes, and tensors
+    that are not on a CUDA device (their host pointers would reach the
+    kernels).  The library is replaced by a stub that fails the test if it is
+    called at all; CPU tensors suffice because the device check comes last."""
+    import torch
+    from lm_head_projection_amd import functional, linear_cross_entropy
+
+    def no_library(*a, **k):
+        raise AssertionError("the library was called before the arguments were checked")
+
+    for name in ("load", "lce_compact_valid", "lce_forward_ex", "lce_backward_ex", "lce_forward_workspace_size",
+                 "lce_workspace_size"):
+        monkeypatch.setattr(functional._lib, name, no_library)
+    H = torch.zeros(4, 8)
+    W = torch.zeros(5, 8)
+    y = torch.zeros(4, dtype=torch.int64)
+    cases = [
+        (dict(hidden=H, weight=torch.zeros(5, 6), labels=y), ValueError),             # D mismatch
+        (dict(hidden=H, weight=W, labels=torch.zeros(3, dtype=torch.int64)), ValueError),  # labels != N
+        (dict(hidden=H, weight=W, labels=y, mask=torch.ones(5, dtype=torch.bool)), ValueError),
+        (dict(hidden=H, weight=W, labels=y, bias=torch.zeros(4)), ValueError),         # bias != V
+        (dict(hidden=H, weight=W, labels=y, bias=torch.zeros(5, 1)), ValueError),
+        (dict(hidden=H, weight=W, labels=y, reduction="sum", loss_weights=torch.ones(3)), ValueError),
+        (dict(hidden=H, weight=W, labels=y, reduction="mean", loss_weights=torch.ones(4)), ValueError),
+        (dict(hidden=H, weight=W.to(torch.bfloat16), labels=y), TypeError),            # mixed dtypes
+        (dict(hidden=H, weight=W, labels=y, bias=torch.zeros(5, dtype=torch.float64)), TypeError),
+        (dict(hidden=H.double(), weight=W.double(), labels=y), TypeError),             # unsupported dtype
+        (dict(hidden=H, weight=W, labels=torch.zeros(4)), TypeError),                  # float labels
+        (dict(hidden=H, weight=W, labels=y, filter_eps=-1.0), ValueError),
+        (dict(hidden=H, weight=W, labels=y, filter_eps=float("nan")), ValueError),
+        (dict(hidden=H, weight=W, labels=y, filter_eps=0.1), TypeError),              # filter needs bf16
+        (dict(hidden=H, weight=W, labels=y, reduction="sum", num_label_tokens=-2.0), ValueError),
+        (dict(hidden=H, weight=torch.zeros(0, 8), labels=y), ValueError),             # V = 0
+        (dict(hidden=H, weight=W, labels=y), ValueError),                              # host tensors
+    ]
+    for kwargs, exc in cases:
+        with pytest.raises(exc):
+            linear_cross_entropy(**kwargs)
+
+
+def test_forward_workspace_is_the_forward_part_of_the_workspace(lib):
+    """The compaction and forward calls need only a forward part of the
+    workspace: far smaller than the whole (which holds one chunk of G and the
+    dH accumulators), never larger, 0 for invalid sizes."""
+    BF16, F32 = _lib.LCE_DTYPE_BF16, _lib.LCE_DTYPE_F32
+    assert lib.lce_forward_workspace_size(-1, 8, 8, BF16) == 0
+    assert lib.lce_forward_workspace_size(8, 8, 8, 7) == 0
+    for N, D, V, dt in ((16384, 1024, 248320, BF16), (32768, 4096, 248320, BF16), (2048, 1024, 151936, BF16),
+                        (64, 128, 1000, F32), (1, 8, 1, BF16)):
+        f = lib.lce_forward_workspace_size(N, D, V, dt)
+        w = lib.lce_workspace_size(N, D, V, dt)
+        esz = 2 if dt == BF16 else 4
+        assert 0 < f <= w
+        # gathered rows (N x D) plus at most 1 KB of partials and indices per position
+        assert f <= (N + 256) * D * esz + (N + 256) * 1024 + 65536, (N, D, V, f)
+    assert lib.lce_forward_workspace_size(16384, 1024, 248320, BF16) < lib.lce_workspace_size(
+        16384, 1024, 248320, BF16) / 20
