@@ -15,6 +15,8 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import platform
+import statistics
 import subprocess
 import sys
 import time
@@ -119,6 +121,39 @@ def stored_traffic(kernel: str, workload: str):
             "path": os.path.relpath(path, ROOT)}
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def blas_vendor():
+    """The BLAS library NumPy calls (name, version, threads), as threadpoolctl reports it."""
+    try:
+        from threadpoolctl import threadpool_info
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                return {"library": i.get("internal_api"), "version": i.get("version"),
+                        "threads": i.get("num_threads"), "path": os.path.basename(i.get("filepath", ""))}
+    except Exception:
+        pass
+    return None
+
+
+def library_record():
+    """Which HIP library ran: its path (relative to the repository), the
+    SHA-256 of the file and of the sources it is built from."""
+    from lm_head_projection_amd import _lib
+    from lm_head_projection_amd.build import file_digest, source_digest
+    return {"path": os.path.relpath(_lib.LIB_PATH, ROOT), "sha256": file_digest(_lib.LIB_PATH),
+            "source_sha256": source_digest()}
+
+
 def cpu_baseline(wl, target_s: float, forward_only: bool = False):
     """The oracle as it stands, on a bounded sample of supervised rows."""
     import numpy as np
@@ -153,6 +188,7 @@ def cpu_baseline(wl, target_s: float, forward_only: bool = False):
     if n2 > n:
         n, t = n2, run(n2)
     return {"value": n / t, "unit": "supervised tokens/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": cpu_model(), "blas": blas_vendor(), "numpy": np.__version__,
             "sample": f"{n} of {C} supervised rows of the {wl.name} workload (full D={wl.D}, V={wl.V}); "
                       f"float64 NumPy dense {'forward' if forward_only else 'forward+backward'}, {t:.1f} s"}
 
@@ -274,21 +310,24 @@ def main():
     if not train:
         log("[bench] forward-only: compaction + forward, no saved statistics")
 
-    # Timed region: K steps bracketed by synchronisation; HIP events on the stream.
+    # Timed region: K steps bracketed by synchronisation; HIP events on the
+    # stream, one between every two steps (per-step times for the median).
     torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs[0].record(stream)
     wall0 = time.perf_counter()
-    for _ in range(args.steps):
+    for i in range(args.steps):
         C = step()
-    ev1.record(stream)
+        evs[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    total_ms = ev0.elapsed_time(ev1)
+    total_ms = evs[0].elapsed_time(evs[-1])
     ms = total_ms / args.steps
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+    step_ms = {"mean": ms, "median": statistics.median(per_step), "min": per_step[0], "max": per_step[-1]}
     peak_extra = torch.cuda.max_memory_allocated() - base_alloc
-    log(f"[bench] {args.steps} steps: {ms:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f} ms/step), C={C}")
+    log(f"[bench] {args.steps} steps: {ms:.3f} ms/step (median {step_ms['median']:.3f}, min {step_ms['min']:.3f}, "
+        f"max {step_ms['max']:.3f}; wall {wall * 1e3 / args.steps:.3f} ms/step), C={C}")
 
     # Per-kernel durations: the same K steps again, with the library recording
     # a HIP event pair around each of its launches on the launch stream.
@@ -363,6 +402,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "step_ms": step_ms,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -384,6 +424,8 @@ def main():
         "roofline": rf,
         "kernels": kernels,
         "cpu_baseline": cpu,
+        "library": library_record(),
+        "inputs_sha256": wl.sha256(),
         "git": git_rev(),
         "device": torch.cuda.get_device_name(0),
         "torch": torch.__version__,
