@@ -409,6 +409,39 @@ def rows_grad_h(H_rows, W, b, y_rows, scale: float):
     return out
 
 
+def cols_grad(H, W, b, labels, m, logs, cols, lam: float = 1.0, mask=None,
+              ignore_index: int = IGNORE_INDEX, row_block: Optional[int] = None,
+              row_factor: Optional[np.ndarray] = None):
+    """Rows `cols` of dW and entries `cols` of db (glenzli.com section 04:
+    dW_j = sum_i G_ij H_i, db_j = sum_i G_ij) from the saved statistics m and
+    log s of every supervised row, for checks at sizes where the whole dW is
+    out of reach: only the score columns Z[:, cols] are formed.  Rows are
+    scaled by lam / C, or by row_factor[i] when it is given."""
+    H = _f64(H)
+    W = _f64(W)
+    b = _f64(b)
+    cols = np.asarray(cols, dtype=np.int64)
+    a, idx, C = supervised_rows(labels, mask, ignore_index)
+    check_labels(labels, idx, W.shape[0])
+    y = np.asarray(labels, dtype=np.int64)
+    dW = np.zeros((cols.size, H.shape[1]))
+    db = np.zeros(cols.size)
+    if C == 0:
+        return dW, db
+    Wc = W[cols]
+    bc = None if b is None else b[cols]
+    for lo, hi in _row_blocks(C, row_block):
+        rows = idx[lo:hi]
+        Z = logits(H[rows], Wc, bc)
+        P = np.exp((Z - m[rows][:, None]) - logs[rows][:, None])
+        P -= (y[rows][:, None] == cols[None, :]).astype(np.float64)
+        r = np.full(rows.size, lam / C) if row_factor is None else np.asarray(row_factor, dtype=np.float64)[rows]
+        G = r[:, None] * P
+        dW += G.T @ H[rows]
+        db += G.sum(axis=0)
+    return dW, db
+
+
 def tiled_forward_backward(H, W, b, labels, mask=None, lam: float = 1.0, T: int = 16,
                            B: int = 256, ignore_index: int = IGNORE_INDEX, _fault: str = ""):
     """The page's tile algorithm in float64 (pins the merge identity only).

@@ -386,6 +386,42 @@ def test_row_helpers_match_dense():
     np.testing.assert_allclose(dh, g.dH[rows], rtol=1e-12, atol=1e-18)
 
 
+def test_cols_grad_matches_dense_and_closed_form():
+    """cols_grad (chosen rows of dW and entries of db from the saved
+    statistics) equals the same rows of the dense backward, with and without
+    a bias, mask and per-row factors, in row blocks with a ragged tail; and,
+    at W = b = 0, the closed form dW_j = (lam/C) sum_i (1/V - 1[y_i = j]) H_i,
+    db_j = (lam/C)(C/V - n_j)."""
+    rng = np.random.default_rng(31)
+    N, D, V = 23, 6, 41
+    H = rng.normal(size=(N, D))
+    W = rng.normal(size=(V, D)) * 0.7
+    b = rng.normal(size=V)
+    y = rng.integers(0, V, N)
+    y[[2, 9]] = O.IGNORE_INDEX
+    mask = rng.random(N) > 0.2
+    cols = np.array([0, 5, int(y[0]), int(y[3]), V - 1])
+    for bias, mk in ((b, None), (None, mask)):
+        f = O.dense_forward(H, W, bias, y, mk)
+        g = O.dense_backward(H, W, bias, y, f.m, f.logs, 1.7, mk)
+        dW, db = O.cols_grad(H, W, bias, y, f.m, f.logs, cols, 1.7, mk, row_block=4)
+        np.testing.assert_allclose(dW, g.dW[cols], rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(db, g.db[cols], rtol=1e-12, atol=1e-14)
+    rf = O.row_factors(N, f.idx, f.C, "sum", 0.5, rng.uniform(0, 2, N), 7.0)
+    g = O.dense_backward(H, W, None, y, f.m, f.logs, mask=mask, row_factor=rf)
+    dW, _ = O.cols_grad(H, W, None, y, f.m, f.logs, cols, mask=mask, row_factor=rf)
+    np.testing.assert_allclose(dW, g.dW[cols], rtol=1e-12, atol=1e-14)
+    # closed form at W = b = 0: p = 1/V for every supervised row
+    W0 = np.zeros((V, D))
+    f = O.dense_forward(H, W0, None, y)
+    dW, db = O.cols_grad(H, W0, None, y, f.m, f.logs, cols, 2.0)
+    sup = f.idx
+    for k, j in enumerate(cols):
+        want = (2.0 / f.C) * ((1.0 / V - (y[sup] == j)) [:, None] * H[sup]).sum(axis=0)
+        np.testing.assert_allclose(dW[k], want, rtol=1e-12, atol=1e-14)
+        assert abs(db[k] - (2.0 / f.C) * (f.C / V - np.sum(y[sup] == j))) < 1e-13
+
+
 def test_row_block_is_only_a_memory_bound():
     wl = WL.make_workload("page2_small")
     H, W, b = wl.H.double().numpy(), wl.W.double().numpy(), wl.b.double().numpy()
