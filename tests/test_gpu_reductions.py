@@ -94,16 +94,34 @@ def test_mean_ex_is_bitwise_the_plain_entry():
 
 
 @pytest.mark.parametrize("red", ["mean", "sum", "none"])
-def test_forward_only_without_saved_statistics(red):
-    """The evaluation entry: m and logs NULL; the loss bits equal those of the
-    run that saves the statistics."""
-    wl = WL.make_workload("sft_small")
-    w = np.linspace(0.5, 1.5, wl.N).astype(np.float32) if red == "sum" else None
+@pytest.mark.parametrize("name", ["tiny", "sft_small", "page2_small"])
+def test_forward_only_without_saved_statistics(name, red):
+    """The evaluation entry (cross-entropy and perplexity without a backward;
+    AIInfraGuide chapter 2, section 5): m and logs NULL.  The loss is the
+    oracle's reduction of its per-row CE, and its bits equal those of the run
+    that saves the statistics."""
+    wl = WL.make_workload(name)
+    w = np.linspace(-0.5, 1.5, wl.N).astype(np.float32) if red == "sum" else None
     num = 100.0 if red == "sum" else 0.0
-    r_stats = run_gpu_ex(wl, red, w, num, backward=False)
     r_eval = run_gpu_ex(wl, red, w, num, stats=False)
     assert r_eval.status_f == _lib.LCE_OK
     assert r_eval.m is None and r_eval.logs is None
+    H, W, b, y, mask = _np(wl)
+    f = O.dense_forward(H, W, b, y, mask, wl.ignore_index)
+    w64 = None if w is None else w.astype(np.float64)
+    ref = O.reduce_rows(f.row_loss, f.idx, f.C, red, w64, num if num else None)
+    t = tol(wl.dtype)
+    if red == "none":
+        a = np.zeros(wl.N, dtype=bool)
+        a[f.idx] = True
+        assert_stat_close("per-position loss", r_eval.loss[a], ref[a], t["stat"])
+        assert np.all(r_eval.loss[~a] == 0.0)
+    else:
+        scale = np.sum(np.abs(w64[f.idx] * f.row_loss[f.idx])) / num if w is not None else abs(ref)
+        assert abs(r_eval.loss[0] - ref) <= t["loss"] * scale, (r_eval.loss[0], ref)
+        if red == "mean":  # perplexity exp(L): relative error of L times L
+            assert abs(math.exp(r_eval.loss[0]) - math.exp(ref)) <= t["loss"] * abs(ref) * 1.01 * math.exp(ref)
+    r_stats = run_gpu_ex(wl, red, w, num, backward=False)
     np.testing.assert_array_equal(r_eval.loss, r_stats.loss)
 
 
