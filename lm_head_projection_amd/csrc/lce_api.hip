@@ -300,9 +300,15 @@ lce_status_t forward_impl(const T* H, const T* W, const T* b, const int64_t* lab
   const int n_split = choose_split(n_rb, n_vt);
   const int n_work = n_rb * n_split;
   const int per_xcd = (int)cdiv(n_work, 8);
-  set_lds_attr<T>((const void*)k_fwd<T>, gemm_lds_bytes<T>());
-  LCE_LAUNCH("k_fwd", (k_fwd<T>), per_xcd * 8, kThreads, gemm_lds_bytes<T>(), s, W, b, Hc, yc, Cpad,
-             (int)D, (int)V, n_rb, n_split, n_vt, n_work, per_xcd, pm, ps, tgt);
+  if (b) {
+    set_lds_attr<T>((const void*)k_fwd<T, true>, gemm_lds_bytes<T>());
+    LCE_LAUNCH("k_fwd", (k_fwd<T, true>), per_xcd * 8, kThreads, gemm_lds_bytes<T>(), s, W, b, Hc, yc, Cpad,
+               (int)D, (int)V, n_rb, n_split, n_vt, n_work, per_xcd, pm, ps, tgt);
+  } else {
+    set_lds_attr<T>((const void*)k_fwd<T, false>, gemm_lds_bytes<T>());
+    LCE_LAUNCH("k_fwd", (k_fwd<T, false>), per_xcd * 8, kThreads, gemm_lds_bytes<T>(), s, W, b, Hc, yc, Cpad,
+               (int)D, (int)V, n_rb, n_split, n_vt, n_work, per_xcd, pm, ps, tgt);
+  }
   if (shard_part) {  // vocabulary shard: the row partials only
     LCE_LAUNCH("k_shard_partial", k_shard_partial, cdiv(C, 256), 256, 0, s, pm, ps, tgt, n_split, Cpad, (int)C, yc,
                (int)V, shard_part, shard_part + C, shard_part + 2 * C);
@@ -360,8 +366,10 @@ lce_status_t backward_impl(const T* H, const T* W, const T* b, const int64_t* la
   const bool filter = filter_eps >= 0.f && filter_which != 0;
   uint8_t* flags = filter ? reinterpret_cast<uint8_t*>(ws + L.flags) : nullptr;
   const int64_t fstride = L.Vc / 32;
-  set_lds_attr<T>((const void*)k_replay<T, false>, replay_lds_bytes<T, false>());
-  set_lds_attr<T>((const void*)k_replay<T, true>, replay_lds_bytes<T, true>());
+  set_lds_attr<T>((const void*)k_replay<T, false, false>, replay_lds_bytes<T, false>());
+  set_lds_attr<T>((const void*)k_replay<T, true, false>, replay_lds_bytes<T, true>());
+  set_lds_attr<T>((const void*)k_replay<T, false, true>, replay_lds_bytes<T, false>());
+  set_lds_attr<T>((const void*)k_replay<T, true, true>, replay_lds_bytes<T, true>());
   set_lds_attr<T>((const void*)k_grad<T>, grad_lds_bytes<T>());
 
   // dH slots: chunk 0 (the widest) fixes their number S and stores every one
@@ -377,17 +385,17 @@ lce_status_t backward_impl(const T* H, const T* W, const T* b, const int64_t* la
       const int tpw = choose_tiles_per_wg(n_rb, vtiles, (int)cdiv(D, sizeof(T) == 2 ? 64 : Cf::BK));
       const int n_work = n_rb * (int)cdiv(vtiles, tpw);
       const int per_xcd = (int)cdiv(n_work, 8);
-      if (filter) {
-        // Every flag of the chunk's tiles is written (0 or 1) by the tile's replay.
-        LCE_LAUNCH("k_replay", (k_replay<T, true>), per_xcd * 8, kThreads, (replay_lds_bytes<T, true>()), s, W, b, Hc,
-                   yc, mc, lsc, rsc, Cpad, (int)D, (int)V, (int)v0, vtiles, tpw, n_rb, n_work, per_xcd, Gc, ldg,
-                   db ? dbp : (float*)nullptr, lddb, flags, fstride, filter_eps,
-                   filter_which == LCE_FILTER_BOTH ? 1 : 0);
-      } else {
-        LCE_LAUNCH("k_replay", (k_replay<T, false>), per_xcd * 8, kThreads, (replay_lds_bytes<T, false>()), s, W, b, Hc,
-                   yc, mc, lsc, rsc, Cpad, (int)D, (int)V, (int)v0, vtiles, tpw, n_rb, n_work, per_xcd, Gc, ldg,
-                   db ? dbp : (float*)nullptr, lddb, (uint8_t*)nullptr, (int64_t)0, 0.f, 0);
-      }
+      // Every flag of the chunk's tiles is written (0 or 1) by the tile's replay.
+#define LCE_REPLAY(FILT, BIAS, flags_, eps_, zd_)                                                              \
+  LCE_LAUNCH("k_replay", (k_replay<T, FILT, BIAS>), per_xcd * 8, kThreads, (replay_lds_bytes<T, FILT>()), s, W, b, \
+             Hc, yc, mc, lsc, rsc, Cpad, (int)D, (int)V, (int)v0, vtiles, tpw, n_rb, n_work, per_xcd, Gc, ldg,   \
+             db ? dbp : (float*)nullptr, lddb, flags_, fstride, eps_, zd_)
+      const int zero_dead = filter_which == LCE_FILTER_BOTH ? 1 : 0;
+      if (filter && b) LCE_REPLAY(true, true, flags, filter_eps, zero_dead);
+      else if (filter) LCE_REPLAY(true, false, flags, filter_eps, zero_dead);
+      else if (b) LCE_REPLAY(false, true, (uint8_t*)nullptr, 0.f, 0);
+      else LCE_REPLAY(false, false, (uint8_t*)nullptr, 0.f, 0);
+#undef LCE_REPLAY
     }
     // K5: dH split so that one dH tile's K matches one dW tile's K (= Cpad).
     if (chunk == 0)

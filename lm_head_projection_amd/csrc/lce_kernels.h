@@ -309,8 +309,8 @@ __device__ __forceinline__ void fwd_epilogue(f32x16_t (&acc)[Geo<T>::TM][Geo<T>:
   }
 }
 
-template <typename T>
-__global__ __launch_bounds__(kThreads) void k_fwd(const T* __restrict__ W, const T* __restrict__ bias,
+template <typename T, bool HAS_BIAS>
+__global__ __launch_bounds__(kThreads) void k_fwd(const T* __restrict__ W, const T* __restrict__ bias_arg,
                                                   const T* __restrict__ Hc,
                                                   const int* __restrict__ yc, int Cpad, int D, int V,
                                                   int n_rb, int n_split, int n_vt, int n_work,
@@ -319,6 +319,8 @@ __global__ __launch_bounds__(kThreads) void k_fwd(const T* __restrict__ W, const
   using C = Cfg<T>;
   using G = Geo<T>;
   extern __shared__ __align__(16) char smem_raw[];
+  // Without a bias the instantiation carries no bias state through the tile loop.
+  const T* __restrict__ bias = HAS_BIAS ? bias_arg : nullptr;
   const int w = xcd_remap(blockIdx.x, per_xcd);
   if (w >= n_work) return;
   int rb, split;
@@ -343,7 +345,7 @@ __global__ __launch_bounds__(kThreads) void k_fwd(const T* __restrict__ W, const
   float* red;
   if constexpr (sizeof(T) == 2) {
     f32x16_t acc[G::TM][G::TN];
-    pipe::run<0, true>(
+    pipe::run<0, true, 0, HAS_BIAS>(
         t1 - t0, nsteps, D, smem_raw, acc,
         [&](int t, pipe::Opnd& A, pipe::Opnd& B, int& k0) {
           A = pipe::Opnd{W, (int64_t)V * D, D, (t0 + t) * C::BM};
@@ -768,9 +770,9 @@ __device__ __forceinline__ void replay_epilogue(f32x16_t (&acc)[Geo<T>::TM][Geo<
   }
 }
 
-template <typename T, bool FILTER = false>
+template <typename T, bool FILTER, bool HAS_BIAS>
 __global__ __launch_bounds__(kThreads) void k_replay(
-    const T* __restrict__ W, const T* __restrict__ bias, const T* __restrict__ Hc,
+    const T* __restrict__ W, const T* __restrict__ bias_arg, const T* __restrict__ Hc,
     const int* __restrict__ yc, const float* __restrict__ mc, const float* __restrict__ lsc,
     const float* __restrict__ rsc, int Cpad,
     int D, int V, int v0, int vtiles, int tpw, int n_rb, int n_work, int per_xcd, T* __restrict__ Gc,
@@ -779,6 +781,7 @@ __global__ __launch_bounds__(kThreads) void k_replay(
   using C = Cfg<T>;
   using G = Geo<T>;
   extern __shared__ __align__(16) char smem_raw[];
+  const T* __restrict__ bias = HAS_BIAS ? bias_arg : nullptr;
   const int w = xcd_remap(blockIdx.x, per_xcd);
   if (w >= n_work) return;
   int rb, vg;
@@ -806,7 +809,7 @@ __global__ __launch_bounds__(kThreads) void k_replay(
     // Each wave's epilogue ends with TN*TM*2 G-tile stores (plus, with a
     // bias, the db stores of some waves and, with the filter, the flag stores
     // of some).
-    pipe::run<0, true, G::TN * G::TM * 2>(
+    pipe::run<0, true, G::TN * G::TM * 2, HAS_BIAS>(
         ntiles, nsteps, D, smem_raw, acc,
         [&](int t, pipe::Opnd& A, pipe::Opnd& B, int& k0) {
           A = pipe::Opnd{W, (int64_t)V * D, D, v0 + (vt0 + t) * C::BM};

@@ -265,12 +265,12 @@ __device__ __forceinline__ void zero(f32x16_t (&acc)[TM][TN]) {
 // issues (an undercount is safe: the first stage wait after an epilogue then
 // also drains some of them).  Vector memory operations retire in issue order
 // on this target, so those younger stores need not be waited for.
-// With `bias` (A K-contiguous, A.r0 = the tile's first vocabulary row),
+// With HAS_BIAS and `bias` (A K-contiguous, A.r0 = the tile's first vocabulary row),
 // wave 0 also loads each tile's 256 bias values into bias_slice(lds, t),
 // right before that tile's first stage: the stage wait that publishes the
 // stage publishes the slice too.  A slot is reloaded 4 tiles later, after
 // the barriers that follow the last epilogue that read it.
-template <int A_MODE, bool B_KC, int EPI_STORES = 0, typename Origin, typename Epi>
+template <int A_MODE, bool B_KC, int EPI_STORES = 0, bool HAS_BIAS = false, typename Origin, typename Epi>
 __device__ __forceinline__ void run(int ntiles, int nsteps, int kend, char* lds, f32x16_t (&acc)[TM][TN],
                                     Origin origin, Epi epi, bool a_kc = true,
                                     const uint16_t* bias = nullptr, int V = 0) {
@@ -298,7 +298,7 @@ __device__ __forceinline__ void run(int ntiles, int nsteps, int kend, char* lds,
   plan_tile(0);
   auto issue_next = [&](int g) {
     char* st = lds + (g & 1) * STAGE_BYTES;
-    if (bias != nullptr && is == 0 && wave_s == 0) {
+    if (HAS_BIAS && is == 0 && wave_s == 0) {
       const __amdgpu_buffer_rsrc_t rb = make_rsrc(bias + bias_m0, (int64_t)(V - bias_m0) * 2);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(lds + BIAS_OFFSET + (it & (BIAS_SLOTS - 1)) * BIAS_SLOT_BYTES),
                                                16, (uint32_t)lane * 16, 0, 0, 0);
