@@ -59,7 +59,9 @@ typedef enum {
   LCE_ERR_LABEL = -2,      /* a supervised label lies outside [0, V) */
   LCE_ERR_WORKSPACE = -3,  /* ws_bytes below the size the call needs */
   LCE_ERR_HIP = -4,        /* a HIP runtime call or kernel launch failed */
-  LCE_ERR_UNSUPPORTED = -5 /* shape outside the documented limits */
+  LCE_ERR_UNSUPPORTED = -5, /* shape outside the documented limits */
+  LCE_ERR_SCRATCH = -6      /* lce_forward_ex_noalloc: the forward workspace
+                               of these sizes exceeds its static scratch */
 } lce_status_t;
 
 /* Reduction of the per-row cross-entropy l_i = log sum_j exp(Z_ij) - Z_{i,y_i}
@@ -162,6 +164,26 @@ lce_status_t lce_forward_ex(const void* H, const void* W, const void* b, const i
                             lce_dtype_t dt, lce_reduction_t reduction, const float* loss_weights,
                             double num_label_tokens, float* loss, float* m, float* logs, void* ws,
                             size_t ws_bytes, void* stream);
+
+/* lce_forward_ex without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  The workspace is a static device
+ * array of the library, 64 MiB on each device the library runs on, held
+ * until the process ends; the call itself allocates nothing.  Sizes whose
+ * forward workspace (lce_forward_workspace_size(N, D, V, dt)) exceeds it are
+ * refused with LCE_ERR_SCRATCH before any HIP call (e.g. N = 16384, D = 1024
+ * fits; N = 32768, D = 4096 does not).  The first call on a device resolves
+ * the array's address on that device (hipGetSymbolAddress), so make it
+ * outside graph capture.  Every call on one device shares that device's
+ * array: calls that overlap in time on one device (different streams or
+ * threads) race and must be serialised by the caller.  The arrays keep the
+ * last call's contents; no call reads what an earlier one left.  Arguments,
+ * outputs and statuses otherwise as for lce_forward_ex, whose kernels it
+ * runs (the results are bit for bit those of lce_forward_ex). */
+lce_status_t lce_forward_ex_noalloc(const void* H, const void* W, const void* b, const int64_t* labels,
+                                    const int32_t* valid_idx, int64_t C, int64_t N, int64_t D, int64_t V,
+                                    lce_dtype_t dt, lce_reduction_t reduction, const float* loss_weights,
+                                    double num_label_tokens, float* loss, float* m, float* logs, void* stream);
 
 /* Backward pass for a chosen reduction (section 04 with the row factor of
  * that reduction): G_ij = r_i (p_ij - 1[j = y_i]) on supervised rows, with

@@ -23,6 +23,7 @@ LCE_ERR_LABEL = -2
 LCE_ERR_WORKSPACE = -3
 LCE_ERR_HIP = -4
 LCE_ERR_UNSUPPORTED = -5
+LCE_ERR_SCRATCH = -6
 
 LCE_REDUCTION_MEAN = 0
 LCE_REDUCTION_SUM = 1
@@ -39,6 +40,7 @@ EXPORTS = (
     "lce_forward",
     "lce_backward",
     "lce_forward_ex",
+    "lce_forward_ex_noalloc",
     "lce_backward_ex",
     "lce_backward_filtered",
     "lce_forward_shard",
@@ -85,6 +87,9 @@ def load() -> ctypes.CDLL:
     lib.lce_forward_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
                                    ctypes.c_int, vp, dbl, vp, vp, vp, vp, sz, vp]
     lib.lce_forward_ex.restype = ctypes.c_int
+    lib.lce_forward_ex_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
+                                           ctypes.c_int, vp, dbl, vp, vp, vp, vp]
+    lib.lce_forward_ex_noalloc.restype = ctypes.c_int
     lib.lce_backward_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
                                     ctypes.c_int, vp, dbl, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.lce_backward_ex.restype = ctypes.c_int
@@ -180,6 +185,16 @@ def lce_forward_ex(H, W, b, labels, valid_idx, C: int, reduction: int, loss_weig
                                  dtype_code(H.dtype), int(reduction), _ptr(loss_weights),
                                  float(num_label_tokens), _ptr(loss), _ptr(m), _ptr(logs), _ptr(ws),
                                  ws.numel(), _stream_ptr(stream))
+
+
+def lce_forward_ex_noalloc(H, W, b, labels, valid_idx, C: int, reduction: int, loss_weights,
+                           num_label_tokens: float, loss, m, logs, stream=None) -> int:
+    N, D = H.shape
+    V = W.shape[0]
+    return load().lce_forward_ex_noalloc(_ptr(H), _ptr(W), _ptr(b), _ptr(labels), _ptr(valid_idx), C, N, D, V,
+                                         dtype_code(H.dtype), int(reduction), _ptr(loss_weights),
+                                         float(num_label_tokens), _ptr(loss), _ptr(m), _ptr(logs),
+                                         _stream_ptr(stream))
 
 
 def lce_backward_ex(H, W, b, labels, valid_idx, C: int, reduction: int, loss_weights,

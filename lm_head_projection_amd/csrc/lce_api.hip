@@ -529,6 +529,32 @@ lce_status_t backward_entry(const void* H, const void* W, const void* b, const i
   }
 }
 
+// ------------------------------------------------------------------ static scratch
+// The no-allocation entry's workspace: a file-scope device array that every
+// device the library runs on holds until the process ends.  Host code never
+// passes the array's name to a kernel (on the host it is only a stand-in for
+// the symbol): the device address of each device's copy is resolved once, on
+// the first call on that device, with that device current.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_ptr;  // per device: the address of its `scratch`
+
+lce_status_t scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return LCE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if ((size_t)dev >= g_scratch_ptr.size()) g_scratch_ptr.resize((size_t)dev + 1, nullptr);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return LCE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return LCE_OK;
+}
+
 }  // namespace
 
 // ====================================================================== C ABI
@@ -555,6 +581,7 @@ const char* lce_status_string(lce_status_t st) {
     case LCE_ERR_WORKSPACE: return "workspace too small";
     case LCE_ERR_HIP: return "HIP runtime error";
     case LCE_ERR_UNSUPPORTED: return "unsupported shape";
+    case LCE_ERR_SCRATCH: return "problem too large for the 64 MiB static scratch of the no-allocation entry";
   }
   return "unknown status";
 }
@@ -619,6 +646,34 @@ lce_status_t lce_forward_ex(const void* H, const void* W, const void* b, const i
                          ws_bytes, stream);
   return forward_entry(H, W, b, labels, valid_idx, C, N, D, V, dt, red, loss, m, logs, nullptr, ws,
                        ws_bytes, stream);
+}
+
+lce_status_t lce_forward_ex_noalloc(const void* H, const void* W, const void* b, const int64_t* labels,
+                                    const int32_t* valid_idx, int64_t C, int64_t N, int64_t D, int64_t V,
+                                    lce_dtype_t dt, lce_reduction_t reduction, const float* loss_weights,
+                                    double num_label_tokens, float* loss, float* m, float* logs, void* stream) {
+  try {
+    Reduce red;
+    LCE_TRY(make_reduce(reduction, loss_weights, num_label_tokens, red));
+    if (!loss || !dims_ok(N, D, V, dt) || C < 0 || C > N) return LCE_ERR_ARG;
+    // Size check first: a problem whose forward workspace exceeds the scratch
+    // is refused before any HIP call.
+    Layout L;
+    if (!make_layout(N, D, V, dt, L)) return LCE_ERR_ARG;
+    if (L.fwd_total > kScratchBytes) return LCE_ERR_SCRATCH;
+    void* ws = nullptr;
+    LCE_TRY(scratch_address(&ws));
+    // The forward kernels write every workspace element they later read
+    // (gathered rows, split partials, targets of supervised rows, row CE), so
+    // the scratch needs no clearing between calls.
+    if (red.kind == kReduceNone)
+      return forward_entry(H, W, b, labels, valid_idx, C, N, D, V, dt, red, nullptr, m, logs, loss, ws,
+                           kScratchBytes, stream);
+    return forward_entry(H, W, b, labels, valid_idx, C, N, D, V, dt, red, loss, m, logs, nullptr, ws, kScratchBytes,
+                         stream);
+  } catch (...) {
+    return LCE_ERR_HIP;
+  }
 }
 
 lce_status_t lce_backward(const void* H, const void* W, const void* b, const int64_t* labels,

@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for st in (0, 1, -1, -2, -3, -4, -5):
+    for st in (0, 1, -1, -2, -3, -4, -5, -6):
         assert lib.lce_status_string(st)
     assert b"C == 0" in lib.lce_status_string(1)
 
@@ -122,7 +122,8 @@ def test_host_argument_checks_return_before_any_hip_call(lib):
 
 
 def test_python_binding_names_match_c_abi():
-    for n in ("lce_workspace_size", "lce_forward_workspace_size", "lce_compact_valid", "lce_forward", "lce_backward", "lce_forward_ex",
+    for n in ("lce_workspace_size", "lce_forward_workspace_size", "lce_compact_valid", "lce_forward", "lce_backward",
+              "lce_forward_ex", "lce_forward_ex_noalloc",
               "lce_backward_ex", "lce_backward_filtered", "lce_forward_shard", "lce_merge_shards",
               "lce_backward_shard"):
         assert callable(getattr(_lib, n))
@@ -202,3 +203,25 @@ def test_forward_workspace_is_the_forward_part_of_the_workspace(lib):
         assert f <= (N + 256) * D * esz + (N + 256) * 1024 + 65536, (N, D, V, f)
     assert lib.lce_forward_workspace_size(16384, 1024, 248320, BF16) < lib.lce_workspace_size(
         16384, 1024, 248320, BF16) / 20
+
+
+def test_noalloc_forward_refuses_sizes_beyond_its_scratch_before_any_hip_call(lib):
+    """lce_forward_ex_noalloc checks its arguments, then the size of the
+    forward workspace against its 64 MiB static scratch, before any HIP call
+    (null pointers suffice here, since nothing is launched)."""
+    loss = ctypes.c_void_p(16)
+    BF16 = _lib.LCE_DTYPE_BF16
+    f = lib.lce_forward_ex_noalloc
+    # stress sizes: about 290 MB of forward workspace
+    assert lib.lce_forward_workspace_size(32768, 4096, 248320, BF16) > 64 << 20
+    assert f(None, None, None, None, None, 5, 32768, 4096, 248320, BF16, 0, None, 0.0, loss, None, None,
+             None) == _lib.LCE_ERR_SCRATCH
+    # argument errors come first
+    assert f(None, None, None, None, None, 5, 32768, 4096, 248320, BF16, 0, None, 0.0, None, None, None,
+             None) == _lib.LCE_ERR_ARG
+    assert f(None, None, None, None, None, 5, 4, 4096, 248320, BF16, 0, None, 0.0, loss, None, None,
+             None) == _lib.LCE_ERR_ARG
+    assert f(None, None, None, None, None, 1, 4, 8, 8, BF16, 9, None, 0.0, loss, None, None,
+             None) == _lib.LCE_ERR_ARG
+    # the packed sizes fit
+    assert lib.lce_forward_workspace_size(16384, 1024, 248320, BF16) <= 64 << 20
