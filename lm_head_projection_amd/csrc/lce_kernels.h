@@ -1015,9 +1015,9 @@ __global__ __launch_bounds__(kThreads) void k_grad(
       if (nsteps == 0) pipe32::zero(acc);
     }
     if (dh)
-      pipe32::run<0, false>(1, nsteps, kend, smem_raw, acc, origin, no_epi, true, nullptr, 0, kmap);
+      pipe32::run<0, false>(1, nsteps, kend, smem_raw, acc, origin, no_epi, true, kmap);
     else
-      pipe32::run<1, false>(1, nsteps, kend, smem_raw, acc, origin, no_epi, true, nullptr, 0, kmap);
+      pipe32::run<1, false>(1, nsteps, kend, smem_raw, acc, origin, no_epi, true, kmap);
     grad_store<T>(acc, dh, m0, n0, D, vc, v0, slot, accumulate, dW);
   } else {
     T* smem = reinterpret_cast<T*>(smem_raw);

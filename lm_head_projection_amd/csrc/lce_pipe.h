@@ -156,9 +156,12 @@ __device__ __forceinline__ void plan_opnd(Plan& p, const Opnd& o, int k0, int wa
 
 // Issues this wave's share (DMA_PER_OPND x 1 KB) of one stage; krel = k of
 // the stage relative to the tile's k0.  K-contiguous chunks at or past krel_end
-// load 0 (only checked when the stage straddles it).
+// load 0 (only checked when the stage straddles it).  With `live` false every
+// chunk takes an offset past the operand, so the hardware writes zeros into
+// the slot: the issue has no branch and its loads can be scheduled among MFMAs.
 template <bool KC>
-__device__ __forceinline__ void issue_plan(const Plan& p, int krel, int krel_end, char* lds_opnd, int wave) {
+__device__ __forceinline__ void issue_plan(const Plan& p, int krel, int krel_end, char* lds_opnd, int wave,
+                                           bool live = true) {
   // Blocked K-outer: a stage stays inside one 256-row block (stages are 64
   // rows, blocks 256), so the stage offset is block base + row offset.
   uint32_t add = (uint32_t)krel * p.kstride;
@@ -171,7 +174,8 @@ __device__ __forceinline__ void issue_plan(const Plan& p, int krel, int krel_end
     // precomputed per-lane offsets held across the loop).
     const uint32_t u = __builtin_amdgcn_readfirstlane(p.ub + (uint32_t)i * p.us + add);
     uint32_t off = p.vb[i & 1] + u;
-    if (tail && krel + p.kc8[i & 1] >= krel_end) off = kOobOffset;
+    off = (tail && krel + p.kc8[i & 1] >= krel_end) ? kOobOffset : off;
+    off = live ? off : kOobOffset;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(p.rs, (lds_void*)(lds_opnd + (wave * DMA_PER_OPND + i) * 1024), 16,
                                              off, 0, 0, 0);
   }
@@ -226,17 +230,45 @@ struct Frags {
                                                               __builtin_bit_cast(bf16x8_t, b[tn]),
                                                               acc[tm][tn], 0, 0, 0);
   }
+  // First substep of a tile: the sums start from zero in the MFMA.
+  __device__ __forceinline__ void mma0(f32x16_t (&acc)[TM][TN]) const {
+    const f32x16_t z = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn)
+        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[tm]),
+                                                              __builtin_bit_cast(bf16x8_t, b[tn]), z, 0, 0, 0);
+  }
   // LDS read instructions per substep (a transposed fragment takes two).
   static constexpr int kReads = TM * (A_MODE == 0 ? 1 : 2) + TN * (B_KC ? 1 : 2);
 };
 
-// Interleaves a substep's R LDS reads with its M MFMAs in the schedule.
+// Schedule of one substep's M MFMAs and the R fragment reads (of the next
+// substep) issued among them: the reads go out between the first MFMAs, so
+// they have the remaining MFMAs' time to land (R > M puts several reads
+// after one MFMA).
 template <int R, int M>
-__device__ __forceinline__ void interleave() {
-  if constexpr (R > 0) {
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, M / R, 0);
-    interleave<R - 1, M - M / R>();
+__device__ __forceinline__ void front_reads() {
+  if constexpr (R > 0 && M > 0) {
+    constexpr int r = (R + M - 1) / M;
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, r, 0);
+    front_reads<R - r, M - 1>();
+  } else if constexpr (M > 0) {
+    __builtin_amdgcn_sched_group_barrier(0x008, M, 0);
+  }
+}
+// The substep that follows a stage barrier: the DMA instructions of a later
+// stage (Q) and the next substep's fragment reads (R) among its M MFMAs.
+template <int Q, int R, int M>
+__device__ __forceinline__ void front_dma_reads() {
+  if constexpr (M > 0 && (Q > 0 || R > 0)) {
+    constexpr int q = (Q + M - 1) / M, r = (R + M - 1) / M;
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (q > 0) __builtin_amdgcn_sched_group_barrier(0x020, q, 0);
+    if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);
+    front_dma_reads<Q - q, R - r, M - 1>();
   } else if constexpr (M > 0) {
     __builtin_amdgcn_sched_group_barrier(0x008, M, 0);
   }
@@ -258,9 +290,9 @@ __device__ __forceinline__ void zero(f32x16_t (&acc)[TM][TN]) {
 //   epi(t, acc): consumes tile t's accumulator (registers; may use the LDS
 //   scratch after the ring, with raw_barrier + wait_lgkm0 for its own sync).
 // On return no load is in flight and every wave has passed a final barrier.
-// `acc` belongs to the caller: it is zeroed at the start of every tile and,
-// after the call, holds the last tile's sums (single-tile callers store it
-// themselves after run() instead of inside the pipelined loop).
+// `acc` belongs to the caller; the first substep of every tile overwrites it
+// (its MFMAs start from zero) and, after the call, it holds the last tile's
+// sums (single-tile callers store it themselves after run()).
 // EPI_STORES: vector memory operations every wave's epilogue certainly
 // issues (an undercount is safe: the first stage wait after an epilogue then
 // also drains some of them).  Vector memory operations retire in issue order
@@ -270,6 +302,17 @@ __device__ __forceinline__ void zero(f32x16_t (&acc)[TM][TN]) {
 // right before that tile's first stage: the stage wait that publishes the
 // stage publishes the slice too.  A slot is reloaded 4 tiles later, after
 // the barriers that follow the last epilogue that read it.
+//
+// Schedule.  Per stage g (slot g & 1), substeps 0..2 each read the next
+// substep's fragments among their first MFMAs; the compiler's own waits hold
+// an MFMA until its fragments have landed, and a scheduling fence keeps each
+// substep's MFMAs ahead of the next substep's.  After substep 2 every wave has
+// its reads of slot g done (lgkm wait) and its loads of stage g+1 landed (vm
+// wait); the barrier makes both true for the workgroup, so during substep 3
+// slot g takes stage g+2 (DMA) and stage g+1's first fragments are read, both
+// among substep 3's MFMAs.  Past the last stage these loads take an offset
+// past the operand (zeros into a free slot) and the reads fetch values nobody
+// uses, so no branch splits the substep.
 template <int A_MODE, bool B_KC, int EPI_STORES = 0, bool HAS_BIAS = false, typename Origin, typename Epi>
 __device__ __forceinline__ void run(int ntiles, int nsteps, int kend, char* lds, f32x16_t (&acc)[TM][TN],
                                     Origin origin, Epi epi, bool a_kc = true,
@@ -296,25 +339,31 @@ __device__ __forceinline__ void run(int ntiles, int nsteps, int kend, char* lds,
     plan_opnd<B_KC>(pB, B, k0, wave_s, lane);
   };
   plan_tile(0);
-  auto issue_next = [&](int g) {
+  auto issue = [&](int g, bool live) {
     char* st = lds + (g & 1) * STAGE_BYTES;
-    if (HAS_BIAS && is == 0 && wave_s == 0) {
+    if (HAS_BIAS && is == 0 && wave_s == 0 && live) {
       const __amdgpu_buffer_rsrc_t rb = make_rsrc(bias + bias_m0, (int64_t)(V - bias_m0) * 2);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(lds + BIAS_OFFSET + (it & (BIAS_SLOTS - 1)) * BIAS_SLOT_BYTES),
                                                16, (uint32_t)lane * 16, 0, 0, 0);
     }
-    if constexpr (A_MODE == 0) issue_plan<true>(pA, is * BK, kend, st, wave_s);
-    else if constexpr (A_MODE == 1) issue_plan<false>(pA, is * BK, kend, st, wave_s);
-    else if (a_kc) issue_plan<true>(pA, is * BK, kend, st, wave_s);
-    else issue_plan<false>(pA, is * BK, kend, st, wave_s);
-    issue_plan<B_KC>(pB, is * BK, kend, st + OPND_BYTES, wave_s);
+    if constexpr (A_MODE == 0) issue_plan<true>(pA, is * BK, kend, st, wave_s, live);
+    else if constexpr (A_MODE == 1) issue_plan<false>(pA, is * BK, kend, st, wave_s, live);
+    else if (a_kc) issue_plan<true>(pA, is * BK, kend, st, wave_s, live);
+    else issue_plan<false>(pA, is * BK, kend, st, wave_s, live);
+    issue_plan<B_KC>(pB, is * BK, kend, st + OPND_BYTES, wave_s, live);
+  };
+  auto advance = [&]() {
     if (++is == nsteps) {
       is = 0;
       if (++it < ntiles) plan_tile(it);
     }
   };
-  issue_next(0);
-  if (total > 1) issue_next(1);
+  issue(0, true);
+  advance();
+  if (total > 1) {
+    issue(1, true);
+    advance();
+  }
   // Stage 0 must have landed (stage 1 may stay in flight).
   if (total > 1) wait_vmcnt<DMA_PER_STAGE>();
   else wait_vmcnt<0>();
@@ -322,29 +371,23 @@ __device__ __forceinline__ void run(int ntiles, int nsteps, int kend, char* lds,
   F x, y;
   x.load(lds, 0, wm, wn, lane, a_kc);
 
-  // Per stage g (slot g & 1): substeps 0..2 each wait for their fragments,
-  // read the next substep's and run their MFMAs.  Before substep 3's MFMAs
-  // each wave has finished its reads of slot g (lgkm wait) and has its loads
-  // of stage g+1 landed (vm wait); the barrier makes both true for the whole
-  // workgroup, so slot g then takes stage g+2 and the first fragments of
-  // stage g+1 are read.
   for (int t = 0; t < ntiles; ++t) {
-    zero(acc);
     for (int s = 0; s < nsteps; ++s) {
       const int g = t * nsteps + s;
       const char* st = lds + (g & 1) * STAGE_BYTES;
-      wait_lgkm0();
       y.load(st, 1, wm, wn, lane, a_kc);
-      x.mma(acc);
-      interleave<F::kReads, TM * TN>();
-      wait_lgkm0();
+      if (s == 0) x.mma0(acc);
+      else x.mma(acc);
+      front_reads<F::kReads, TM * TN>();
+      __builtin_amdgcn_sched_barrier(0);
       x.load(st, 2, wm, wn, lane, a_kc);
       y.mma(acc);
-      interleave<F::kReads, TM * TN>();
-      wait_lgkm0();
+      front_reads<F::kReads, TM * TN>();
+      __builtin_amdgcn_sched_barrier(0);
       y.load(st, 3, wm, wn, lane, a_kc);
       x.mma(acc);
-      interleave<F::kReads, TM * TN>();
+      front_reads<F::kReads, TM * TN>();
+      __builtin_amdgcn_sched_barrier(0);
       wait_lgkm0();
       if (g + 1 < total) {
         // Stage g+1 must have landed; the stores of an epilogue that ran
@@ -353,13 +396,19 @@ __device__ __forceinline__ void run(int ntiles, int nsteps, int kend, char* lds,
         else wait_vmcnt<0>();
       }
       raw_barrier();
-      if (g + 2 < total) issue_next(g + 2);
-      if (g + 1 < total) x.load(lds + ((g + 1) & 1) * STAGE_BYTES, 0, wm, wn, lane, a_kc);
+      const bool more2 = g + 2 < total;
+      issue(g + 2, more2);
+      x.load(lds + ((g + 1) & 1) * STAGE_BYTES, 0, wm, wn, lane, a_kc);
       y.mma(acc);
-      interleave<F::kReads, TM * TN>();
+      front_dma_reads<DMA_PER_STAGE, F::kReads, TM * TN>();
+      __builtin_amdgcn_sched_barrier(0);
+      if (more2) advance();
     }
     epi(t, acc);
   }
+  // The last two stages issued loads past the operand: they must have
+  // written their zeros before the workgroup's LDS can be reused.
+  wait_vmcnt<0>();
   wait_lgkm0();
   raw_barrier();
 }

@@ -6,8 +6,10 @@
 // same operand descriptions (pipe::Opnd) as lce_pipe.h.
 //
 // Operand tiles travel global -> LDS with `buffer_load_dwordx4 ... lds` (no
-// staging registers) through a ring of NS = 4 LDS stages of BK = 32: three
-// stages are in flight while one is consumed.  Each wave waits only for its
+// staging registers) through a ring of NS = 4 LDS stages of BK = 32: while a
+// stage is consumed the next one has landed and the one after it is in
+// flight, and the slot freed at the previous barrier takes the stage after
+// those.  Each wave waits only for its
 // own loads (vmcnt) and one workgroup barrier per stage publishes the stage
 // and frees the slot that the next load overwrites.
 //
@@ -33,14 +35,8 @@ constexpr int OPND_BYTES = 256 * BK * 2;          // one operand, one stage: 16 
 constexpr int STAGE_BYTES = 2 * OPND_BYTES;       // A then B
 constexpr int RING_BYTES = NS * STAGE_BYTES;      // 128 KB
 constexpr int SCRATCH_BYTES = 4096;               // epilogue scratch after the ring
-constexpr int BIAS_SLOTS = 4, BIAS_SLOT_BYTES = 1024;  // per-tile bias slices after the scratch
-constexpr int BIAS_OFFSET = RING_BYTES + SCRATCH_BYTES;
-constexpr int LDS_BYTES = BIAS_OFFSET + BIAS_SLOTS * BIAS_SLOT_BYTES;
+constexpr int LDS_BYTES = RING_BYTES + SCRATCH_BYTES + 4096;  // the BK=64 pipeline's footprint
 
-// LDS copy of the bias slice of tile t (element j = bias[m0(t) + j], 0 past V).
-__device__ __forceinline__ const uint16_t* bias_slice(const char* lds, int t) {
-  return reinterpret_cast<const uint16_t*>(lds + BIAS_OFFSET + (t & (BIAS_SLOTS - 1)) * BIAS_SLOT_BYTES);
-}
 constexpr int WGM = 2, WGN = 4, WTM = 128, WTN = 64, TM = 4, TN = 2;
 constexpr int DMA_PER_OPND = OPND_BYTES / 1024 / 8;  // 1 KB DMA instructions per wave: 2
 constexpr int DMA_PER_STAGE = 2 * DMA_PER_OPND;      // 4 per wave per stage
@@ -54,18 +50,6 @@ using pipe::raw_barrier;
 using pipe::v4i16;
 using pipe::wait_lgkm0;
 using pipe::wait_vmcnt;
-
-// Waits until at most `n` vector memory operations are outstanding, for the
-// n this pipeline produces: k*DMA_PER_STAGE (k = 0..2) plus optionally `extra`
-// younger operations (stores an epilogue issued after those loads).
-template <int EXTRA>
-__device__ __forceinline__ void wait_vmcnt_rt(int n) {
-  if (n >= 2 * DMA_PER_STAGE + EXTRA) wait_vmcnt<2 * DMA_PER_STAGE + EXTRA>();
-  else if (n >= DMA_PER_STAGE + EXTRA) wait_vmcnt<DMA_PER_STAGE + EXTRA>();
-  else if (n >= 2 * DMA_PER_STAGE) wait_vmcnt<2 * DMA_PER_STAGE>();
-  else if (n >= DMA_PER_STAGE) wait_vmcnt<DMA_PER_STAGE>();
-  else wait_vmcnt<0>();
-}
 
 // ------------------------------------------------------------------ loads
 // Per-tile load plan of one operand: a buffer resource at the tile origin
@@ -123,7 +107,8 @@ __device__ __forceinline__ void plan_opnd(Plan& p, const Opnd& o, int k0, int wa
 // the stage relative to the tile's k0.  K-contiguous chunks at or past krel_end
 // load 0 (only checked when the stage straddles it).
 template <bool KC>
-__device__ __forceinline__ void issue_plan(const Plan& p, int krel, int krel_end, char* lds_opnd, int wave) {
+__device__ __forceinline__ void issue_plan(const Plan& p, int krel, int krel_end, char* lds_opnd, int wave,
+                                           bool live = true) {
   // Blocked K-outer: a stage stays inside one 256-row block (stages are 32
   // rows, blocks 256), so the stage offset is block base + row offset.
   uint32_t add = (uint32_t)krel * p.kstride;
@@ -133,7 +118,8 @@ __device__ __forceinline__ void issue_plan(const Plan& p, int krel, int krel_end
 #pragma unroll
   for (int i = 0; i < DMA_PER_OPND; ++i) {
     uint32_t off = p.voff[i] + add;
-    if (tail && krel + p.kc8[i] >= krel_end) off = kOobOffset;
+    off = (tail && krel + p.kc8[i] >= krel_end) ? kOobOffset : off;
+    off = live ? off : kOobOffset;  // no branch: see pipe::issue_plan
     __builtin_amdgcn_raw_ptr_buffer_load_lds(p.rs, (lds_void*)(lds_opnd + (wave * DMA_PER_OPND + i) * 1024), 16,
                                              off, 0, 0, 0);
   }
@@ -187,6 +173,15 @@ struct Frags {
                                                               __builtin_bit_cast(bf16x8_t, b[tn]),
                                                               acc[tm][tn], 0, 0, 0);
   }
+  __device__ __forceinline__ void mma0(f32x16_t (&acc)[TM][TN]) const {
+    const f32x16_t z = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn)
+        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[tm]),
+                                                              __builtin_bit_cast(bf16x8_t, b[tn]), z, 0, 0, 0);
+  }
   static constexpr int kReads = (TM * (A_MODE == 0 ? 1 : 2)) + TN * (B_KC ? 1 : 2);
 };
 
@@ -205,27 +200,34 @@ __device__ __forceinline__ void zero(f32x16_t (&acc)[TM][TN]) {
 //   (relative to the same origin as k0 + s*BK);
 //   epi(t, acc): consumes tile t's accumulator (registers; may use the LDS
 //   scratch after the ring, with raw_barrier + wait_lgkm0 for its own sync).
+//   Stores an epilogue issues inside the walk only make later stage waits
+//   drain more (the waits count every vector memory operation in order).
 // On return no load is in flight and every wave has passed a final barrier.
-// `acc` belongs to the caller: it is zeroed at the start of every tile and,
-// after the call, holds the last tile's sums (single-tile callers store it
-// themselves after run() instead of inside the pipelined loop).
-// EPI_STORES: vector memory operations every wave's epilogue certainly
-// issues after its last load wait (an undercount is safe: the wait after an
-// epilogue then also drains some of them).  Vector memory operations retire
-// in issue order on this target, so younger stores need not be waited for.
-// With `bias` (A K-contiguous, A.r0 = the tile's first vocabulary row),
-// wave 0 also loads each tile's 256 bias values into bias_slice(lds, t),
-// right before that tile's first stage: the stage wait that publishes the
-// stage publishes the slice too.  A slot is reloaded 4 tiles later, after the
-// barrier that follows the last epilogue that read it ((4-1)*nsteps >= 3).
+// `acc` belongs to the caller: the first substep of every tile overwrites it
+// (its MFMAs start from zero); after the call it holds the last tile's sums
+// (single-tile callers store it themselves after run()).  With nsteps = 0 it
+// is left untouched.
 // kmap (optional, LDS, single-tile runs): the stages to run, as indices of
 // BK-wide k steps from k0; stage s loads k = k0 + kmap[s]*BK (the other
 // steps are skipped, as if their operand tiles were zero).
-template <int A_MODE, bool B_KC, int EPI_STORES = 0, typename Origin, typename Epi>
+//
+// Schedule.  Stage g sits in slot g % NS.  While stage g is consumed, stage
+// g+1 has landed and stage g+2 is in flight.  Per stage: substep 0 reads
+// substep 1's fragments among its first MFMAs; then each wave waits for its
+// reads of slot g and its loads of stage g+1, and the barrier makes both true
+// for the workgroup; substep 1 then issues stage g+3 into slot g-1 (free
+// since the previous barrier) and reads stage g+1's first fragments, both
+// among its MFMAs.  Stages past the end load zeros (constant counts, no
+// branch).
+// The explicit vmcnt waits order every LDS read after the DMA that fills its
+// slot.  A stage's body takes its three slots (read now, read next, filled)
+// as distinct restrict pointers, which they are, so that the compiler does
+// not also drain every DMA in flight before each transposing LDS read.
+template <int A_MODE, bool B_KC, typename Origin, typename Epi>
 __device__ __forceinline__ void run(int ntiles, int nsteps, int kend, char* lds, f32x16_t (&acc)[TM][TN],
-                                    Origin origin, Epi epi, bool a_kc = true,
-                                    const uint16_t* bias = nullptr, int V = 0, const int* kmap = nullptr) {
-  static_assert(BK == 32, "Frags covers the two 16-wide k-substeps of a stage");
+                                    Origin origin, Epi epi, bool a_kc = true, const int* kmap = nullptr) {
+  static_assert(BK == 32 && NS == 4, "two 16-wide k-substeps per stage, four slots");
+  using F = Frags<A_MODE, B_KC>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave % WGM, wn = wave / WGM;
   const int total = ntiles * nsteps;
@@ -233,12 +235,10 @@ __device__ __forceinline__ void run(int ntiles, int nsteps, int kend, char* lds,
   // Issue state (the next global step to load).
   int it = 0, is = 0;
   Plan pA, pB;
-  int bias_m0 = 0;
   auto plan_tile = [&](int t) {
     Opnd A, B;
     int k0;
     origin(t, A, B, k0);
-    bias_m0 = A.r0;
     if constexpr (A_MODE == 0) plan_opnd<true>(pA, A, k0, wave_s, lane);
     else if constexpr (A_MODE == 1) plan_opnd<false>(pA, A, k0, wave_s, lane);
     else if (a_kc) plan_opnd<true>(pA, A, k0, wave_s, lane);
@@ -246,57 +246,64 @@ __device__ __forceinline__ void run(int ntiles, int nsteps, int kend, char* lds,
     plan_opnd<B_KC>(pB, B, k0, wave_s, lane);
   };
   plan_tile(0);
-  auto issue_next = [&](int g) {
-    char* st = lds + (g % NS) * STAGE_BYTES;
-    if (bias != nullptr && is == 0 && wave_s == 0) {
-      const __amdgpu_buffer_rsrc_t rb = make_rsrc(bias + bias_m0, (int64_t)(V - bias_m0) * 2);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(lds + BIAS_OFFSET + (it & (BIAS_SLOTS - 1)) * BIAS_SLOT_BYTES),
-                                               16, (uint32_t)lane * 16, 0, 0, 0);
-    }
-    const int kr = (kmap ? __builtin_amdgcn_readfirstlane(kmap[is]) : is) * BK;
-    if constexpr (A_MODE == 0) issue_plan<true>(pA, kr, kend, st, wave_s);
-    else if constexpr (A_MODE == 1) issue_plan<false>(pA, kr, kend, st, wave_s);
-    else if (a_kc) issue_plan<true>(pA, kr, kend, st, wave_s);
-    else issue_plan<false>(pA, kr, kend, st, wave_s);
-    issue_plan<B_KC>(pB, kr, kend, st + OPND_BYTES, wave_s);
+  auto issue = [&](char* st, const int* km, bool live) {
+    const int kr = live ? (km ? __builtin_amdgcn_readfirstlane(km[is]) : is) * BK : 0;
+    if constexpr (A_MODE == 0) issue_plan<true>(pA, kr, kend, st, wave_s, live);
+    else if constexpr (A_MODE == 1) issue_plan<false>(pA, kr, kend, st, wave_s, live);
+    else if (a_kc) issue_plan<true>(pA, kr, kend, st, wave_s, live);
+    else issue_plan<false>(pA, kr, kend, st, wave_s, live);
+    issue_plan<B_KC>(pB, kr, kend, st + OPND_BYTES, wave_s, live);
+  };
+  auto advance = [&]() {
     if (++is == nsteps) {
       is = 0;
       if (++it < ntiles) plan_tile(it);
     }
   };
 #pragma unroll
-  for (int g = 0; g < NS - 1; ++g)
-    if (g < total) issue_next(g);
+  for (int g = 0; g < NS - 1; ++g) {
+    const bool live = g < total;
+    issue(lds + g * STAGE_BYTES, kmap, live);
+    if (live) advance();
+  }
+  // Stage 0 must have landed (stages 1 and 2 may stay in flight).
+  wait_vmcnt<(NS - 2) * DMA_PER_STAGE>();
+  raw_barrier();
+  F x, y;
+  x.load(lds, 0, wm, wn, lane, a_kc);
 
-  // One barrier per stage: it publishes stage g (each wave waited for its
-  // own loads) and frees the slot of stage g-1 for the load of stage g+3.
-  // Per stage: all LDS fragment reads, then the next loads, then the MFMAs.
+  // One stage: cur = slot g, nxt = slot g+1, dst = slot g+3 (= g-1).
+  auto stage = [&](const char* __restrict__ cur, const char* __restrict__ nxt, char* __restrict__ dst,
+                   const int* __restrict__ km, int g, bool first) {
+    y.load(cur, 1, wm, wn, lane, a_kc);
+    if (first) x.mma0(acc);
+    else x.mma(acc);
+    pipe::front_reads<F::kReads, TM * TN>();
+    __builtin_amdgcn_sched_barrier(0);
+    wait_lgkm0();
+    wait_vmcnt<DMA_PER_STAGE>();  // stage g+1 landed (stage g+2 may stay in flight)
+    raw_barrier();
+    const bool more = g + NS - 1 < total;
+    issue(dst, km, more);
+    x.load(nxt, 0, wm, wn, lane, a_kc);
+    y.mma(acc);
+    pipe::front_dma_reads<DMA_PER_STAGE, F::kReads, TM * TN>();
+    __builtin_amdgcn_sched_barrier(0);
+    if (more) advance();
+  };
   int t = 0, s = 0;
   for (int g = 0; g < total; ++g) {
-    // Stage g must have landed; later stages already issued may stay in
-    // flight, and so may the stores of an epilogue that ran just before.
-    const int later = DMA_PER_STAGE * min(NS - 2, total - 1 - g);
-    if (EPI_STORES > 0 && s == 0 && g > 0 && later > 0)
-      wait_vmcnt_rt<EPI_STORES>(later + EPI_STORES);
-    else
-      wait_vmcnt_rt<0>(later);
-    raw_barrier();
-    if (s == 0) zero(acc);
-    const char* st = lds + (g % NS) * STAGE_BYTES;
-    Frags<A_MODE, B_KC> f0, f1;
-    f0.load(st, 0, wm, wn, lane, a_kc);
-    f1.load(st, 1, wm, wn, lane, a_kc);
-    if (g + NS - 1 < total) issue_next(g + NS - 1);
-    f0.mma(acc);
-    f1.mma(acc);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * Frags<A_MODE, B_KC>::kReads, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 2 * TM * TN, 0);
+    stage(lds + (g & (NS - 1)) * STAGE_BYTES, lds + ((g + 1) & (NS - 1)) * STAGE_BYTES,
+          lds + ((g + NS - 1) & (NS - 1)) * STAGE_BYTES, kmap, g, s == 0);
     if (++s == nsteps) {
       epi(t, acc);
       s = 0;
       ++t;
     }
   }
+  // Loads past the end wrote zeros into free slots: done before the LDS is reused.
+  wait_vmcnt<0>();
+  wait_lgkm0();
   raw_barrier();
 }
 
