@@ -391,9 +391,10 @@ lce_status_t backward_impl(const T* H, const T* W, const T* b, const int64_t* la
              Hc, yc, mc, lsc, rsc, Cpad, (int)D, (int)V, (int)v0, vtiles, tpw, n_rb, n_work, per_xcd, Gc, ldg,   \
              db ? dbp : (float*)nullptr, lddb, flags_, fstride, eps_, zd_)
       const int zero_dead = filter_which == LCE_FILTER_BOTH ? 1 : 0;
-      if (filter && b) LCE_REPLAY(true, true, flags, filter_eps, zero_dead);
+      const bool bias_terms = b != nullptr || db != nullptr;  // a bias to add or db partials to form
+      if (filter && bias_terms) LCE_REPLAY(true, true, flags, filter_eps, zero_dead);
       else if (filter) LCE_REPLAY(true, false, flags, filter_eps, zero_dead);
-      else if (b) LCE_REPLAY(false, true, (uint8_t*)nullptr, 0.f, 0);
+      else if (bias_terms) LCE_REPLAY(false, true, (uint8_t*)nullptr, 0.f, 0);
       else LCE_REPLAY(false, false, (uint8_t*)nullptr, 0.f, 0);
 #undef LCE_REPLAY
     }

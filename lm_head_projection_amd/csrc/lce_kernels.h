@@ -776,12 +776,15 @@ __global__ __launch_bounds__(kThreads) void k_replay(
     const int* __restrict__ yc, const float* __restrict__ mc, const float* __restrict__ lsc,
     const float* __restrict__ rsc, int Cpad,
     int D, int V, int v0, int vtiles, int tpw, int n_rb, int n_work, int per_xcd, T* __restrict__ Gc,
-    int64_t ldg, float* __restrict__ dbp, int64_t lddb, uint8_t* __restrict__ flags = nullptr,
+    int64_t ldg, float* __restrict__ dbp_arg, int64_t lddb, uint8_t* __restrict__ flags = nullptr,
     int64_t fstride = 0, float eps = 0.f, int zero_dead = 0) {
   using C = Cfg<T>;
   using G = Geo<T>;
   extern __shared__ __align__(16) char smem_raw[];
+  // HAS_BIAS: a bias to add or db partials to form (either may still be
+  // absent); without it the instantiation carries neither through the loop.
   const T* __restrict__ bias = HAS_BIAS ? bias_arg : nullptr;
+  float* __restrict__ dbp = HAS_BIAS ? dbp_arg : nullptr;
   const int w = xcd_remap(blockIdx.x, per_xcd);
   if (w >= n_work) return;
   int rb, vg;

@@ -24,6 +24,8 @@
 //    consecutive k of one r.
 #pragma once
 
+#include <type_traits>
+
 #include "lce_device.h"
 
 namespace lce {
@@ -371,39 +373,42 @@ __device__ __forceinline__ void run(int ntiles, int nsteps, int kend, char* lds,
   F x, y;
   x.load(lds, 0, wm, wn, lane, a_kc);
 
-  for (int t = 0; t < ntiles; ++t) {
-    for (int s = 0; s < nsteps; ++s) {
-      const int g = t * nsteps + s;
-      const char* st = lds + (g & 1) * STAGE_BYTES;
-      y.load(st, 1, wm, wn, lane, a_kc);
-      if (s == 0) x.mma0(acc);
-      else x.mma(acc);
-      front_reads<F::kReads, TM * TN>();
-      __builtin_amdgcn_sched_barrier(0);
-      x.load(st, 2, wm, wn, lane, a_kc);
-      y.mma(acc);
-      front_reads<F::kReads, TM * TN>();
-      __builtin_amdgcn_sched_barrier(0);
-      y.load(st, 3, wm, wn, lane, a_kc);
-      x.mma(acc);
-      front_reads<F::kReads, TM * TN>();
-      __builtin_amdgcn_sched_barrier(0);
-      wait_lgkm0();
-      if (g + 1 < total) {
-        // Stage g+1 must have landed; the stores of an epilogue that ran
-        // after its loads were issued may stay in flight.
-        if (EPI_STORES > 0 && s == 0 && t > 0) wait_vmcnt<EPI_STORES>();
-        else wait_vmcnt<0>();
-      }
-      raw_barrier();
-      const bool more2 = g + 2 < total;
-      issue(g + 2, more2);
-      x.load(lds + ((g + 1) & 1) * STAGE_BYTES, 0, wm, wn, lane, a_kc);
-      y.mma(acc);
-      front_dma_reads<DMA_PER_STAGE, F::kReads, TM * TN>();
-      __builtin_amdgcn_sched_barrier(0);
-      if (more2) advance();
+  // One stage; FIRST: the tile's first, whose first substep starts the sums
+  // from zero (a separate copy, so no branch splits the substep schedule).
+  auto stage = [&](int g, auto first) {
+    const char* st = lds + (g & 1) * STAGE_BYTES;
+    y.load(st, 1, wm, wn, lane, a_kc);
+    if constexpr (decltype(first)::value) x.mma0(acc);
+    else x.mma(acc);
+    front_reads<F::kReads, TM * TN>();
+    __builtin_amdgcn_sched_barrier(0);
+    x.load(st, 2, wm, wn, lane, a_kc);
+    y.mma(acc);
+    front_reads<F::kReads, TM * TN>();
+    __builtin_amdgcn_sched_barrier(0);
+    y.load(st, 3, wm, wn, lane, a_kc);
+    x.mma(acc);
+    front_reads<F::kReads, TM * TN>();
+    __builtin_amdgcn_sched_barrier(0);
+    wait_lgkm0();
+    if (g + 1 < total) {
+      // Stage g+1 must have landed; the stores of an epilogue that ran
+      // after its loads were issued may stay in flight.
+      if (EPI_STORES > 0 && decltype(first)::value && g > 0) wait_vmcnt<EPI_STORES>();
+      else wait_vmcnt<0>();
     }
+    raw_barrier();
+    const bool more2 = g + 2 < total;
+    issue(g + 2, more2);
+    x.load(lds + ((g + 1) & 1) * STAGE_BYTES, 0, wm, wn, lane, a_kc);
+    y.mma(acc);
+    front_dma_reads<DMA_PER_STAGE, F::kReads, TM * TN>();
+    __builtin_amdgcn_sched_barrier(0);
+    if (more2) advance();
+  };
+  for (int t = 0; t < ntiles; ++t) {
+    stage(t * nsteps, std::true_type{});
+    for (int s = 1; s < nsteps; ++s) stage(t * nsteps + s, std::false_type{});
     epi(t, acc);
   }
   // The last two stages issued loads past the operand: they must have

@@ -274,9 +274,9 @@ __device__ __forceinline__ void run(int ntiles, int nsteps, int kend, char* lds,
 
   // One stage: cur = slot g, nxt = slot g+1, dst = slot g+3 (= g-1).
   auto stage = [&](const char* __restrict__ cur, const char* __restrict__ nxt, char* __restrict__ dst,
-                   const int* __restrict__ km, int g, bool first) {
+                   const int* __restrict__ km, int g, auto first) {
     y.load(cur, 1, wm, wn, lane, a_kc);
-    if (first) x.mma0(acc);
+    if constexpr (decltype(first)::value) x.mma0(acc);
     else x.mma(acc);
     pipe::front_reads<F::kReads, TM * TN>();
     __builtin_amdgcn_sched_barrier(0);
@@ -291,15 +291,16 @@ __device__ __forceinline__ void run(int ntiles, int nsteps, int kend, char* lds,
     __builtin_amdgcn_sched_barrier(0);
     if (more) advance();
   };
-  int t = 0, s = 0;
-  for (int g = 0; g < total; ++g) {
+  // The tile's first stage is a separate copy (its first substep starts the
+  // sums from zero), so no branch splits the substep schedule.
+  auto run_stage = [&](int g, auto first) {
     stage(lds + (g & (NS - 1)) * STAGE_BYTES, lds + ((g + 1) & (NS - 1)) * STAGE_BYTES,
-          lds + ((g + NS - 1) & (NS - 1)) * STAGE_BYTES, kmap, g, s == 0);
-    if (++s == nsteps) {
-      epi(t, acc);
-      s = 0;
-      ++t;
-    }
+          lds + ((g + NS - 1) & (NS - 1)) * STAGE_BYTES, kmap, g, first);
+  };
+  for (int t = 0; t < ntiles && nsteps > 0; ++t) {
+    run_stage(t * nsteps, std::true_type{});
+    for (int s = 1; s < nsteps; ++s) run_stage(t * nsteps + s, std::false_type{});
+    epi(t, acc);
   }
   // Loads past the end wrote zeros into free slots: done before the LDS is reused.
   wait_vmcnt<0>();
