@@ -1017,10 +1017,22 @@ __global__ __launch_bounds__(kThreads) void k_grad(
       }
       if (nsteps == 0) pipe32::zero(acc);
     }
-    if (dh)
-      pipe32::run<0, false>(1, nsteps, kend, smem_raw, acc, origin, no_epi, true, kmap);
-    else
-      pipe32::run<1, false>(1, nsteps, kend, smem_raw, acc, origin, no_epi, true, kmap);
+    if (kmap != nullptr) {
+      // Filtered: the stage lists skip single 32-wide k steps.
+      if (dh)
+        pipe32::run<0, false>(1, nsteps, kend, smem_raw, acc, origin, no_epi, true, kmap);
+      else
+        pipe32::run<1, false>(1, nsteps, kend, smem_raw, acc, origin, no_epi, true, kmap);
+    } else {
+      // BK = 64 stages (half the barriers); a split whose length is an odd
+      // multiple of 32 ends in a half stage whose K-contiguous G part reads
+      // zeros past kend, so its other half contributes nothing.
+      const int nsteps64 = (nsteps + 1) / 2;
+      if (dh)
+        pipe::run_ko<0, false>(1, nsteps64, kend, smem_raw, acc, origin, no_epi);
+      else
+        pipe::run_ko<1, false>(1, nsteps64, kend, smem_raw, acc, origin, no_epi);
+    }
     grad_store<T>(acc, dh, m0, n0, D, vc, v0, slot, accumulate, dW);
   } else {
     T* smem = reinterpret_cast<T*>(smem_raw);

@@ -418,5 +418,123 @@ __device__ __forceinline__ void run(int ntiles, int nsteps, int kend, char* lds,
   raw_barrier();
 }
 
+// run_ko: run() re-framed for K-outer operands (same contract).
+// Schedule.  One iteration runs from a stage barrier to the next.  After
+// barrier g-1 (every wave done with slot g-1, stage g landed), iteration g
+// issues stage g+1 into slot g-1 and reads stage g's first fragments among
+// the MFMAs of stage g-1's last substep; at the first stage of a tile the
+// previous tile's epilogue follows.  Substeps 0..2 of stage g then each read
+// the next substep's fragments among their first MFMAs (the compiler's own
+// waits hold an MFMA until its fragments have landed; a scheduling fence
+// keeps each substep's MFMAs ahead of the next substep's).  Each wave then
+// waits for its reads of slot g and its loads of stage g+1, and barrier g
+// makes both true for the workgroup.  Past the last stage the loads take an
+// offset past the operand (zeros into a free slot), so no branch splits the
+// schedule.  An iteration reads only slot g and fills only slot g-1: it takes
+// them as distinct restrict pointers, so that the compiler does not also
+// drain every DMA in flight before a transposing LDS read (K-outer operands);
+// the explicit vmcnt waits order each read after the DMA that fills its slot.
+template <int A_MODE, bool B_KC, int EPI_STORES = 0, bool HAS_BIAS = false, typename Origin, typename Epi>
+__device__ __forceinline__ void run_ko(int ntiles, int nsteps, int kend, char* lds, f32x16_t (&acc)[TM][TN],
+                                       Origin origin, Epi epi, bool a_kc = true,
+                                       const uint16_t* bias = nullptr, int V = 0) {
+  static_assert(BK == 64, "four 16-wide k-substeps per stage");
+  using F = Frags<A_MODE, B_KC>;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave % WGM, wn = wave / WGM;
+  const int total = ntiles * nsteps;
+  if (total == 0) return;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform: keeps LDS targets scalar
+  // Issue state (the next global stage to load).
+  int it = 0, is = 0;
+  Plan pA, pB;
+  int bias_m0 = 0;
+  auto plan_tile = [&](int t) {
+    Opnd A, B;
+    int k0;
+    origin(t, A, B, k0);
+    bias_m0 = A.r0;
+    if constexpr (A_MODE == 0) plan_opnd<true>(pA, A, k0, wave_s, lane);
+    else if constexpr (A_MODE == 1) plan_opnd<false>(pA, A, k0, wave_s, lane);
+    else if (a_kc) plan_opnd<true>(pA, A, k0, wave_s, lane);
+    else plan_opnd<false>(pA, A, k0, wave_s, lane);
+    plan_opnd<B_KC>(pB, B, k0, wave_s, lane);
+  };
+  plan_tile(0);
+  auto issue = [&](char* st, bool live) {
+    if (HAS_BIAS && is == 0 && wave_s == 0 && live) {
+      const __amdgpu_buffer_rsrc_t rb = make_rsrc(bias + bias_m0, (int64_t)(V - bias_m0) * 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(lds + BIAS_OFFSET + (it & (BIAS_SLOTS - 1)) * BIAS_SLOT_BYTES),
+                                               16, (uint32_t)lane * 16, 0, 0, 0);
+    }
+    if constexpr (A_MODE == 0) issue_plan<true>(pA, is * BK, kend, st, wave_s, live);
+    else if constexpr (A_MODE == 1) issue_plan<false>(pA, is * BK, kend, st, wave_s, live);
+    else if (a_kc) issue_plan<true>(pA, is * BK, kend, st, wave_s, live);
+    else issue_plan<false>(pA, is * BK, kend, st, wave_s, live);
+    issue_plan<B_KC>(pB, is * BK, kend, st + OPND_BYTES, wave_s, live);
+  };
+  auto advance = [&]() {
+    if (++is == nsteps) {
+      is = 0;
+      if (++it < ntiles) plan_tile(it);
+    }
+  };
+  issue(lds, true);
+  advance();
+  wait_vmcnt<0>();  // stage 0 landed
+  raw_barrier();
+  F x, y;
+  // Iteration g: cur = slot g, dst = slot g+1 (= g-1).  FIRST: the tile's
+  // first stage (its first substep starts the sums from zero; the previous
+  // tile's epilogue runs first).  PREV: stage g-1's last substep is pending.
+  auto iter = [&](const char* __restrict__ cur, char* __restrict__ dst, int g, int t, auto first, auto prev) {
+    constexpr bool kFirst = decltype(first)::value, kPrev = decltype(prev)::value;
+    const bool live = g + 1 < total;
+    issue(dst, live);
+    x.load(cur, 0, wm, wn, lane, a_kc);
+    if constexpr (kPrev) {
+      y.mma(acc);
+      front_dma_reads<DMA_PER_STAGE, F::kReads, TM * TN>();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (live) advance();
+    if constexpr (kFirst && kPrev) epi(t - 1, acc);
+    y.load(cur, 1, wm, wn, lane, a_kc);
+    if constexpr (kFirst) x.mma0(acc);
+    else x.mma(acc);
+    front_reads<F::kReads, TM * TN>();
+    __builtin_amdgcn_sched_barrier(0);
+    x.load(cur, 2, wm, wn, lane, a_kc);
+    y.mma(acc);
+    front_reads<F::kReads, TM * TN>();
+    __builtin_amdgcn_sched_barrier(0);
+    y.load(cur, 3, wm, wn, lane, a_kc);
+    x.mma(acc);
+    front_reads<F::kReads, TM * TN>();
+    __builtin_amdgcn_sched_barrier(0);
+    wait_lgkm0();
+    // Stage g+1 must have landed; the stores of an epilogue that ran after
+    // its loads were issued may stay in flight.
+    if (kFirst && kPrev && EPI_STORES > 0) wait_vmcnt<EPI_STORES>();
+    else wait_vmcnt<0>();
+    raw_barrier();
+  };
+  auto slot = [&](int g) { return lds + (g & 1) * STAGE_BYTES; };
+  iter(slot(0), slot(1), 0, 0, std::true_type{}, std::false_type{});
+  for (int s = 1; s < nsteps; ++s) iter(slot(s), slot(s + 1), s, 0, std::false_type{}, std::true_type{});
+  for (int t = 1; t < ntiles; ++t) {
+    const int g0 = t * nsteps;
+    iter(slot(g0), slot(g0 + 1), g0, t, std::true_type{}, std::true_type{});
+    for (int s = 1; s < nsteps; ++s) iter(slot(g0 + s), slot(g0 + s + 1), g0 + s, t, std::false_type{}, std::true_type{});
+  }
+  y.mma(acc);  // the last stage's last substep
+  epi(ntiles - 1, acc);
+  // The last stage issued loads past the operand: they must have written
+  // their zeros before the workgroup's LDS can be reused.
+  wait_vmcnt<0>();
+  wait_lgkm0();
+  raw_barrier();
+}
+
 }  // namespace pipe
 }  // namespace lce
