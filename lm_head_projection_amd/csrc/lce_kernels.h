@@ -610,10 +610,11 @@ __device__ __forceinline__ void replay_epilogue(f32x16_t (&acc)[Geo<T>::TM][Geo<
       smask[tn] = 0u;
       sgn[tn] = 1.f;
     } else {
-      // |r| p = exp2(Z log2e - m log2e - (log s log2e - log2 |r|)); r = 0 gives
-      // 0.  The row's constants come from LDS (written once per workgroup).
+      // |r| p = exp2(Z log2e - c) with c = (m + log s) log2e - log2 |r| (one
+      // constant per row, so one FMA per entry); r = 0 gives c = +inf and 0.
+      // The row's constants come from LDS (written once per workgroup).
       const float4 st = rowstat[wn * G::WTN + tn * 32 + (lane & 31)];
-      const float ml = st.x, ll = st.y, rr = st.z;
+      const float c = st.x, rr = st.z;
       const float ar = fabsf(rr);
       yrow[tn] = __float_as_int(st.w);
       absr[tn] = ar;
@@ -621,7 +622,7 @@ __device__ __forceinline__ void replay_epilogue(f32x16_t (&acc)[Geo<T>::TM][Geo<
       for (int tm = 0; tm < G::TM; ++tm)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          acc[tm][tn][i] = __builtin_amdgcn_exp2f(fmaf(acc[tm][tn][i], kLog2e, -ml) - ll);
+          acc[tm][tn][i] = __builtin_amdgcn_exp2f(fmaf(acc[tm][tn][i], kLog2e, -c));
       sub = ar;
       const bool neg = (__float_as_uint(rr) >> 31) != 0u;
       smask[tn] = neg ? 0x80008000u : 0u;
@@ -804,7 +805,7 @@ __global__ __launch_bounds__(kThreads) void k_replay(
     if (threadIdx.x < C::BN) {
       const int r = n0 + threadIdx.x;
       const float rr = rsc[r];
-      rowstat[threadIdx.x] = float4{mc[r] * kLog2e, lsc[r] * kLog2e - log2f(fabsf(rr)), rr,
+      rowstat[threadIdx.x] = float4{fmaf(mc[r], kLog2e, lsc[r] * kLog2e) - log2f(fabsf(rr)), 0.f, rr,
                                     __int_as_float(yc[r])};
     }
     pipe::wait_lgkm0();  // published by the pipeline's first barrier
