@@ -76,11 +76,11 @@ def git_rev():
         return None
 
 
-# Algorithmic FLOPs per step, by kernel (2*C*D*V per GEMM pass).
-def kernel_flops(C, D, V, mode="train"):
-    if mode == "forward":
-        return {"k_fwd": 2.0 * C * D * V}
-    return {"k_fwd": 2.0 * C * D * V, "k_replay": 2.0 * C * D * V, "k_grad": 4.0 * C * D * V}
+# Algorithmic FLOPs per step (2*C*D*V per GEMM pass: the logits in the
+# forward, their replay and the dH and dW products in the backward).  The
+# library reports each launch's share; their sum must come to this.
+def step_flops(C, D, V, mode="train"):
+    return (2.0 if mode == "forward" else 8.0) * C * D * V
 
 
 def kernel_bytes(C, N, D, V, esz, has_mask, has_bias):
@@ -358,28 +358,31 @@ def main():
     flops_step = (8.0 if train else 2.0) * C * D * V
     tflops = flops_step / (ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if wl.dtype == torch.bfloat16 else PEAK_FP32_TFLOPS
-    kf = kernel_flops(C, D, V, args.mode)
-    if args.filter_eps is not None:
-        kf.pop("k_grad")  # the filter skips a data-dependent part of its products
+    lib_flops = sum(v[2] for v in kern.values()) / args.steps
+    if abs(lib_flops - step_flops(C, D, V, args.mode)) > 1e-6 * step_flops(C, D, V, args.mode):
+        log(f"[bench] warning: the library's per-launch flops sum to {lib_flops:.6g} per step, "
+            f"not {step_flops(C, D, V, args.mode):.6g}")
     kb = kernel_bytes(C, N, D, V, 2 if wl.dtype == torch.bfloat16 else 4, mask is not None, b is not None)
     kernels = {}
-    for name, (tot, n) in sorted(kern.items(), key=lambda kv: -kv[1][0]):
+    for name, (tot, n, fl) in sorted(kern.items(), key=lambda kv: -kv[1][0]):
         e = {"total_ms_per_step": tot / args.steps, "launches_per_step": n / args.steps,
              "avg_ms": tot / max(n, 1)}
-        if name in kf:
-            e["tflops"] = kf[name] * args.steps / (tot * 1e-3) / 1e12
+        # The filter skips a data-dependent part of the gradient products: no rate for those launches.
+        if fl > 0 and not (args.filter_eps is not None and name.startswith("k_grad")):
+            e["flops_per_step"] = fl / args.steps
+            e["tflops"] = fl / (tot * 1e-3) / 1e12
         if name in kb:
             e["hbm_gbps"] = kb[name] / (e["avg_ms"] * 1e-3) / 1e9
             if name == "k_dh_finalize":
                 e["hbm_gbps_lower_bound"] = True
         kernels[name] = e
-    dom = max((k for k in kernels if k in kf), key=lambda k: kernels[k]["total_ms_per_step"])
+    dom = max((k for k in kernels if "tflops" in kernels[k]), key=lambda k: kernels[k]["total_ms_per_step"])
     tr = stored_traffic(dom, args.workload)
     rf = {"bound": "mfma", "achieved": kernels[dom]["tflops"], "peak": peak, "unit": "TFLOP/s",
           "frac": kernels[dom]["tflops"] / peak,
           "traffic": None if tr is None else tr["fetch_bytes_per_launch"] + tr["write_bytes_per_launch"],
           "kernel": dom,
-          "flops_per_launch": kf[dom] / kernels[dom]["launches_per_step"],
+          "flops_per_launch": kernels[dom]["flops_per_step"] / kernels[dom]["launches_per_step"],
           "avg_launch_ms": kernels[dom]["avg_ms"],
           "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
           "traffic_source": None if tr is None else tr["path"]}

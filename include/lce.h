@@ -80,10 +80,21 @@ typedef enum {
 
 /* Bytes of device workspace that lce_compact_valid, lce_forward and
  * lce_backward need for these sizes (worst case C = N).  It never grows with
- * N x V: the largest pieces are the gathered supervised rows (N x D), one
- * vocabulary chunk of the softmax-gradient tile store (N x min(V, 32768)) and
- * the fp32 dH accumulators (at most 4 x N x D).  Returns 0 for invalid sizes. */
+ * N x V: the largest pieces are the gathered supervised rows (N x D), the
+ * softmax-gradient tile store (two vocabulary chunks of N x min(V, 32768) for
+ * bf16, one for fp32) and the fp32 dH accumulators (at most 4 x N x D).
+ * Returns 0 for invalid sizes. */
 size_t lce_workspace_size(int64_t N, int64_t D, int64_t V, lce_dtype_t dt);
+
+/* Bytes of device workspace that lce_backward, lce_backward_ex,
+ * lce_backward_filtered and lce_backward_shard need when C of the N rows are
+ * supervised (0 <= C <= N, the count lce_compact_valid returned): the
+ * backward's arrays (two vocabulary chunks of the bf16 softmax-gradient tile
+ * store, C x min(V, 32768) each; the fp32 dH accumulators, at most 4 x C x D;
+ * the row statistics) take C rows, the gathered rows N.  Never more than
+ * lce_workspace_size(N, D, V, dt), which is this size at C = N.  Returns 0
+ * for invalid sizes or C outside [0, N]. */
+size_t lce_backward_workspace_size(int64_t N, int64_t C, int64_t D, int64_t V, lce_dtype_t dt);
 
 /* Bytes of device workspace that the compaction and forward calls alone need
  * (lce_compact_valid, lce_forward, lce_forward_ex, lce_forward_shard with the
@@ -287,13 +298,18 @@ const char* lce_status_string(lce_status_t status);
  * event pair on its stream (up to max_launches launches); lce_profile_stop()
  * synchronises those events and folds them into per-kernel totals, and turns
  * recording off.  lce_profile_count() gives the number of distinct kernels
- * seen; lce_profile_entry(i, ...) copies kernel i's name, total milliseconds
- * and launch count.  Returns LCE_ERR_HIP if an event call fails. */
+ * seen; lce_profile_entry(i, ...) copies kernel i's name, total milliseconds,
+ * launch count and total algorithmic flops (any output pointer may be null).
+ * The flops of a launch are those of the method's products it computes:
+ * 2 C D V_k for the logits of the C supervised rows over a vocabulary range
+ * of V_k entries (k_fwd, k_replay), 4 C D V_k for the dH and dW products of
+ * a chunk (k_grad), the sum of both for k_grad_replay, and 0 for the kernels
+ * outside the GEMMs.  Returns LCE_ERR_HIP if an event call fails. */
 lce_status_t lce_profile_start(int32_t max_launches);
 lce_status_t lce_profile_stop(void);
 int32_t lce_profile_count(void);
 lce_status_t lce_profile_entry(int32_t i, char* name, int32_t name_cap, double* total_ms,
-                               int64_t* launches);
+                               int64_t* launches, double* flops);
 
 #ifdef __cplusplus
 }

@@ -36,6 +36,7 @@ REDUCTIONS = {"mean": LCE_REDUCTION_MEAN, "sum": LCE_REDUCTION_SUM, "none": LCE_
 EXPORTS = (
     "lce_workspace_size",
     "lce_forward_workspace_size",
+    "lce_backward_workspace_size",
     "lce_compact_valid",
     "lce_forward",
     "lce_backward",
@@ -75,6 +76,8 @@ def load() -> ctypes.CDLL:
     lib.lce_workspace_size.restype = sz
     lib.lce_forward_workspace_size.argtypes = [i64, i64, i64, ctypes.c_int]
     lib.lce_forward_workspace_size.restype = sz
+    lib.lce_backward_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.c_int]
+    lib.lce_backward_workspace_size.restype = sz
     lib.lce_compact_valid.argtypes = [vp, vp, i64, i64, i64, vp, ctypes.POINTER(i64), vp, sz, vp]
     lib.lce_compact_valid.restype = ctypes.c_int
     lib.lce_forward.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
@@ -113,7 +116,7 @@ def load() -> ctypes.CDLL:
     lib.lce_profile_count.argtypes = []
     lib.lce_profile_count.restype = i32
     lib.lce_profile_entry.argtypes = [i32, ctypes.c_char_p, i32, ctypes.POINTER(ctypes.c_double),
-                                      ctypes.POINTER(i64)]
+                                      ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_double)]
     lib.lce_profile_entry.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -149,6 +152,10 @@ def lce_workspace_size(N: int, D: int, V: int, dtype) -> int:
 
 def lce_forward_workspace_size(N: int, D: int, V: int, dtype) -> int:
     return int(load().lce_forward_workspace_size(N, D, V, dtype_code(dtype)))
+
+
+def lce_backward_workspace_size(N: int, C: int, D: int, V: int, dtype) -> int:
+    return int(load().lce_backward_workspace_size(N, C, D, V, dtype_code(dtype)))
 
 
 def lce_compact_valid(labels, mask, V: int, ignore_index: int, valid_idx, ws, stream=None):
@@ -257,7 +264,9 @@ def profile_start(max_launches: int = 65536) -> None:
 
 
 def profile_stop() -> dict:
-    """Stops recording; returns {kernel: (total_ms, launches)}."""
+    """Stops recording; returns {kernel: (total_ms, launches, flops)}, flops
+    being the launches' algorithmic floating-point operations (0 outside the
+    GEMM kernels)."""
     lib = load()
     st = lib.lce_profile_stop()
     if st != LCE_OK:
@@ -267,6 +276,7 @@ def profile_stop() -> dict:
     for i in range(lib.lce_profile_count()):
         ms = ctypes.c_double(0)
         n = ctypes.c_int64(0)
-        lib.lce_profile_entry(i, buf, 128, ctypes.byref(ms), ctypes.byref(n))
-        out[buf.value.decode()] = (ms.value, n.value)
+        fl = ctypes.c_double(0)
+        lib.lce_profile_entry(i, buf, 128, ctypes.byref(ms), ctypes.byref(n), ctypes.byref(fl))
+        out[buf.value.decode()] = (ms.value, n.value, fl.value)
     return out

@@ -26,7 +26,7 @@ namespace {
 
 constexpr int64_t kVcMax = 32768;    // vocabulary chunk of the gradient tile store
 constexpr int kMaxSplit = 64;         // vocabulary splits of the forward pass
-constexpr int kDhSlotRows = 4;        // the dH slots hold 4 x Npad rows of D fp32 values
+constexpr int kDhSlotRows = 4;        // the dH slots hold 4 x Rpad rows of D fp32 values
 constexpr int kMaxDhSlots = 16;       // k-splits of the dH GEMM (at most)
 constexpr int kCUs = 256;             // MI355X compute units (one 512-thread workgroup each)
 
@@ -38,17 +38,22 @@ size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 struct Prof {
   bool on = false;
   int max = 0, used = 0, pending_kid = -1;
+  double pending_flops = 0.0;
   std::vector<hipEvent_t> ev;
   std::vector<int> kid;
+  std::vector<double> lflops;  // per recorded launch
   std::vector<std::string> names;
-  std::vector<double> ms;
+  std::vector<double> ms, flops;
   std::vector<int64_t> cnt;
 };
 Prof g_prof;
 
-void prof_begin(const char* name, hipStream_t s) {
+// flops: the launch's algorithmic floating-point operations (0 for the
+// kernels outside the GEMMs).
+void prof_begin(const char* name, hipStream_t s, double flops = 0.0) {
   Prof& p = g_prof;
   p.pending_kid = -1;
+  p.pending_flops = flops;
   if (!p.on || p.used >= p.max) return;
   int id = -1;
   for (size_t i = 0; i < p.names.size(); ++i)
@@ -57,6 +62,7 @@ void prof_begin(const char* name, hipStream_t s) {
     id = (int)p.names.size();
     p.names.push_back(name);
     p.ms.push_back(0.0);
+    p.flops.push_back(0.0);
     p.cnt.push_back(0);
   }
   if (hipEventRecord(p.ev[2 * p.used], s) != hipSuccess) return;
@@ -67,14 +73,18 @@ void prof_end(hipStream_t s) {
   if (p.pending_kid < 0) return;
   if (hipEventRecord(p.ev[2 * p.used + 1], s) == hipSuccess) {
     p.kid[p.used] = p.pending_kid;
+    p.lflops[p.used] = p.pending_flops;
     p.used++;
   }
   p.pending_kid = -1;
 }
 
-#define LCE_LAUNCH(name, kernel, grid, block, shmem, stream, ...)                  \
+#define LCE_LAUNCH(name, kernel, grid, block, shmem, stream, ...) \
+  LCE_LAUNCH_F(name, 0.0, kernel, grid, block, shmem, stream, __VA_ARGS__)
+// A GEMM launch, with its algorithmic flops for the profiler.
+#define LCE_LAUNCH_F(name, flops, kernel, grid, block, shmem, stream, ...)         \
   do {                                                                             \
-    prof_begin(name, stream);                                                      \
+    prof_begin(name, stream, flops);                                               \
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(block), shmem, stream, __VA_ARGS__); \
     hipError_t e_ = hipGetLastError();                                             \
     prof_end(stream);                                                              \
@@ -106,20 +116,26 @@ struct Layout {
   size_t fwd_total;  // compaction + forward calls
   size_t total;      // every call (the backward region is the larger one)
   int64_t Npad, Vpad, Vc, nblk;
+  int64_t Rpad;  // rows of the backward arrays: the supervised rows, padded to 256
 };
 
-bool make_layout(int64_t N, int64_t D, int64_t V, lce_dtype_t dt, Layout& L) {
+// rows: the supervised rows C the backward region serves (0 <= C <= N), or -1
+// for the worst case C = N.  The compaction, shared and forward regions are
+// sized by N.
+bool make_layout(int64_t N, int64_t D, int64_t V, lce_dtype_t dt, Layout& L, int64_t rows = -1) {
   if (N < 0 || D <= 0 || V <= 0) return false;
   if (dt != LCE_DTYPE_F32 && dt != LCE_DTYPE_BF16) return false;
+  if (rows > N) return false;
   const int64_t esz = dt == LCE_DTYPE_BF16 ? 2 : 4;
   const int64_t bn = dt == LCE_DTYPE_BF16 ? Tile<uint16_t>::BN : Tile<float>::BN;
   L.Npad = rup(std::max<int64_t>(N, 1), 256);
+  L.Rpad = rows < 0 ? L.Npad : rup(std::max<int64_t>(rows, 1), 256);
   L.nblk = cdiv(std::max<int64_t>(N, 1), kCmpBlock);
   L.Vpad = rup(V, 256);
   L.Vc = std::min<int64_t>(L.Vpad, kVcMax);
   // The GEMM operands are addressed with 32-bit buffer offsets from a tile
-  // origin: keep one chunk of G (Npad x Vc) and of W (Vc x D) within 2 GB.
-  const int64_t vc_cap = std::min(((int64_t)1 << 31) / (L.Npad * esz), ((int64_t)1 << 31) / (D * esz)) / 256 * 256;
+  // origin: keep one chunk of G (Rpad x Vc) and of W (Vc x D) within 2 GB.
+  const int64_t vc_cap = std::min(((int64_t)1 << 31) / (L.Rpad * esz), ((int64_t)1 << 31) / (D * esz)) / 256 * 256;
   if (vc_cap < 256) return false;
   L.Vc = std::min(L.Vc, vc_cap);
   size_t off = 0;
@@ -144,14 +160,17 @@ bool make_layout(int64_t N, int64_t D, int64_t V, lce_dtype_t dt, Layout& L) {
   L.fwd_total = fwd_end;
   // backward region overlays the forward region (the calls never overlap)
   off = common_end;
-  L.mc = take(L.Npad * 4);
-  L.lsc = take(L.Npad * 4);
-  L.rsc = take(L.Npad * 4);
+  L.mc = take(L.Rpad * 4);
+  L.lsc = take(L.Rpad * 4);
+  L.rsc = take(L.Rpad * 4);
   L.inv = take(std::max<int64_t>(N, 1) * 4);
-  L.G = take(L.Npad * L.Vc * esz);
-  L.slots = take((int64_t)kDhSlotRows * L.Npad * D * 4);
-  L.dbp = take((L.Npad / bn) * L.Vpad * 4);
-  L.flags = take((L.Npad / 256) * (L.Vc / 32));  // gradient filter: live G blocks of one chunk
+  // bf16: two chunk buffers of G (and of the filter flags), so that the
+  // replay of chunk c+1 can run inside the gradient launch of chunk c.
+  const int64_t nbuf = dt == LCE_DTYPE_BF16 ? 2 : 1;
+  L.G = take(nbuf * L.Rpad * L.Vc * esz);
+  L.slots = take((int64_t)kDhSlotRows * L.Rpad * D * 4);
+  L.dbp = take((L.Rpad / bn) * L.Vpad * 4);
+  L.flags = take(nbuf * (L.Rpad / 256) * (L.Vc / 32));  // gradient filter: live G blocks of a chunk
   L.total = std::max(off, fwd_end);
   return true;
 }
@@ -214,12 +233,12 @@ int64_t makespan(int64_t n_a, int64_t L_a, int64_t n_b, int64_t L_b) {
 
 // dH k-splits for one chunk: the split count whose grouped launch (dH tiles of
 // K = chunk/S next to dW tiles of K = Cpad) has the shortest makespan.
-// S is bounded by the slot memory: S x Cpad rows must fit in kDhSlotRows x Npad.
-int choose_dh_splits(int64_t kpad, int64_t Cpad, int64_t Npad, int64_t n_dh_tiles_per_split, int64_t n_dw_tiles,
+// S is bounded by the slot memory: S x Cpad rows must fit in kDhSlotRows x Rpad.
+int choose_dh_splits(int64_t kpad, int64_t Cpad, int64_t Rpad, int64_t n_dh_tiles_per_split, int64_t n_dw_tiles,
                      int bk) {
   int best = 1;
   int64_t best_t = INT64_MAX;
-  const int s_max = (int)std::max<int64_t>(1, std::min<int64_t>(kMaxDhSlots, kDhSlotRows * Npad / Cpad));
+  const int s_max = (int)std::max<int64_t>(1, std::min<int64_t>(kMaxDhSlots, kDhSlotRows * Rpad / Cpad));
   for (int S = 1; S <= s_max; ++S) {
     const int64_t ks_len = rup(cdiv(kpad, S), bk);
     const int64_t S_eff = cdiv(kpad, ks_len);
@@ -300,14 +319,15 @@ lce_status_t forward_impl(const T* H, const T* W, const T* b, const int64_t* lab
   const int n_split = choose_split(n_rb, n_vt);
   const int n_work = n_rb * n_split;
   const int per_xcd = (int)cdiv(n_work, 8);
+  const double fwd_flops = 2.0 * (double)C * (double)V * (double)D;  // one logit per (row, entry)
   if (b) {
     set_lds_attr<T>((const void*)k_fwd<T, true>, gemm_lds_bytes<T>());
-    LCE_LAUNCH("k_fwd", (k_fwd<T, true>), per_xcd * 8, kThreads, gemm_lds_bytes<T>(), s, W, b, Hc, yc, Cpad,
-               (int)D, (int)V, n_rb, n_split, n_vt, n_work, per_xcd, pm, ps, tgt);
+    LCE_LAUNCH_F("k_fwd", fwd_flops, (k_fwd<T, true>), per_xcd * 8, kThreads, gemm_lds_bytes<T>(), s, W, b, Hc,
+                 yc, Cpad, (int)D, (int)V, n_rb, n_split, n_vt, n_work, per_xcd, pm, ps, tgt);
   } else {
     set_lds_attr<T>((const void*)k_fwd<T, false>, gemm_lds_bytes<T>());
-    LCE_LAUNCH("k_fwd", (k_fwd<T, false>), per_xcd * 8, kThreads, gemm_lds_bytes<T>(), s, W, b, Hc, yc, Cpad,
-               (int)D, (int)V, n_rb, n_split, n_vt, n_work, per_xcd, pm, ps, tgt);
+    LCE_LAUNCH_F("k_fwd", fwd_flops, (k_fwd<T, false>), per_xcd * 8, kThreads, gemm_lds_bytes<T>(), s, W, b, Hc,
+                 yc, Cpad, (int)D, (int)V, n_rb, n_split, n_vt, n_work, per_xcd, pm, ps, tgt);
   }
   if (shard_part) {  // vocabulary shard: the row partials only
     LCE_LAUNCH("k_shard_partial", k_shard_partial, cdiv(C, 256), 256, 0, s, pm, ps, tgt, n_split, Cpad, (int)C, yc,
@@ -372,46 +392,134 @@ lce_status_t backward_impl(const T* H, const T* W, const T* b, const int64_t* la
   set_lds_attr<T>((const void*)k_replay<T, true, true>, replay_lds_bytes<T, true>());
   set_lds_attr<T>((const void*)k_grad<T>, grad_lds_bytes<T>());
 
+  // Vocabulary chunks of at most L.Vc entries.
+  struct Chunk {
+    int64_t v0;
+    int vc, vtiles, kpad;
+  };
+  std::vector<Chunk> chunks;
+  for (int64_t v0 = 0; v0 < V; v0 += L.Vc) {
+    const int vc = (int)std::min<int64_t>(L.Vc, V - v0);
+    const int vtiles = (int)cdiv(vc, Cf::BM);
+    chunks.push_back(Chunk{v0, vc, vtiles, vtiles * Cf::BM});
+  }
+  // bf16: chunk c+1's replay runs in chunk c's gradient launch (k_grad_replay),
+  // through the other of two G (and flag) buffers.
+  constexpr bool kFuse = sizeof(T) == 2;
+  const int64_t g_elems = (int64_t)L.Rpad * L.Vc;
+  const int64_t f_bytes = (L.Rpad / 256) * (L.Vc / 32);
+  auto gbuf = [&](size_t c) { return Gc + (kFuse ? (int64_t)(c & 1) * g_elems : 0); };
+  auto fbuf = [&](size_t c) { return flags ? flags + (kFuse ? (int64_t)(c & 1) * f_bytes : 0) : flags; };
+  const bool bias_terms = b != nullptr || db != nullptr;  // a bias to add or db partials to form
+  // Every flag of the chunk's tiles is written (0 or 1) by the tile's replay.
+  auto rargs = [&](size_t c) {
+    const Chunk& k = chunks[c];
+    ReplayArgs<T> a;
+    a.W = W;
+    a.bias = b;
+    a.Hc = Hc;
+    a.yc = yc;
+    a.mc = mc;
+    a.lsc = lsc;
+    a.rsc = rsc;
+    a.Cpad = Cpad;
+    a.D = (int)D;
+    a.V = (int)V;
+    a.v0 = (int)k.v0;
+    a.vtiles = k.vtiles;
+    a.tpw = choose_tiles_per_wg(n_rb, k.vtiles, (int)cdiv(D, sizeof(T) == 2 ? 64 : Cf::BK));
+    a.n_rb = n_rb;
+    a.n_work = n_rb * (int)cdiv(k.vtiles, a.tpw);
+    a.per_xcd = (int)cdiv(a.n_work, 8);
+    a.Gc = gbuf(c);
+    a.ldg = ldg;
+    a.dbp = db ? dbp : nullptr;
+    a.lddb = lddb;
+    a.flags = filter ? fbuf(c) : nullptr;
+    a.fstride = fstride;
+    a.eps = filter ? filter_eps : 0.f;
+    a.zero_dead = filter && filter_which == LCE_FILTER_BOTH ? 1 : 0;
+    return a;
+  };
+  auto replay_flops = [&](size_t c) { return 2.0 * (double)C * (double)chunks[c].vc * (double)D; };
+  auto launch_replay = [&](size_t c) -> lce_status_t {
+    const ReplayArgs<T> a = rargs(c);
+    const int grid = a.per_xcd * 8;
+    const double fl = replay_flops(c);
+    if (filter && bias_terms)
+      LCE_LAUNCH_F("k_replay", fl, (k_replay<T, true, true>), grid, kThreads, (replay_lds_bytes<T, true>()), s, a);
+    else if (filter)
+      LCE_LAUNCH_F("k_replay", fl, (k_replay<T, true, false>), grid, kThreads, (replay_lds_bytes<T, true>()), s, a);
+    else if (bias_terms)
+      LCE_LAUNCH_F("k_replay", fl, (k_replay<T, false, true>), grid, kThreads, (replay_lds_bytes<T, false>()), s, a);
+    else
+      LCE_LAUNCH_F("k_replay", fl, (k_replay<T, false, false>), grid, kThreads, (replay_lds_bytes<T, false>()), s,
+                   a);
+    return LCE_OK;
+  };
+
   // dH slots: chunk 0 (the widest) fixes their number S and stores every one
   // of them; later chunks, whose splits never outnumber S, add into theirs.
   // k_dh_finalize sums exactly these S slots.
   int S = 0;
-  for (int64_t v0 = 0, chunk = 0; v0 < V; v0 += L.Vc, ++chunk) {
-    const int vc = (int)std::min<int64_t>(L.Vc, V - v0);
-    const int vtiles = (int)cdiv(vc, Cf::BM);
-    const int kpad = vtiles * Cf::BM;
-    // K4: replay this chunk into G.
-    {
-      const int tpw = choose_tiles_per_wg(n_rb, vtiles, (int)cdiv(D, sizeof(T) == 2 ? 64 : Cf::BK));
-      const int n_work = n_rb * (int)cdiv(vtiles, tpw);
-      const int per_xcd = (int)cdiv(n_work, 8);
-      // Every flag of the chunk's tiles is written (0 or 1) by the tile's replay.
-#define LCE_REPLAY(FILT, BIAS, flags_, eps_, zd_)                                                              \
-  LCE_LAUNCH("k_replay", (k_replay<T, FILT, BIAS>), per_xcd * 8, kThreads, (replay_lds_bytes<T, FILT>()), s, W, b, \
-             Hc, yc, mc, lsc, rsc, Cpad, (int)D, (int)V, (int)v0, vtiles, tpw, n_rb, n_work, per_xcd, Gc, ldg,   \
-             db ? dbp : (float*)nullptr, lddb, flags_, fstride, eps_, zd_)
-      const int zero_dead = filter_which == LCE_FILTER_BOTH ? 1 : 0;
-      const bool bias_terms = b != nullptr || db != nullptr;  // a bias to add or db partials to form
-      if (filter && bias_terms) LCE_REPLAY(true, true, flags, filter_eps, zero_dead);
-      else if (filter) LCE_REPLAY(true, false, flags, filter_eps, zero_dead);
-      else if (bias_terms) LCE_REPLAY(false, true, (uint8_t*)nullptr, 0.f, 0);
-      else LCE_REPLAY(false, false, (uint8_t*)nullptr, 0.f, 0);
-#undef LCE_REPLAY
-    }
+  if (kFuse) LCE_TRY(launch_replay(0));
+  for (size_t c = 0; c < chunks.size(); ++c) {
+    const Chunk& k = chunks[c];
+    // K4: replay this chunk into G (bf16: done by the previous launch).
+    if (!kFuse) LCE_TRY(launch_replay(c));
     // K5: dH split so that one dH tile's K matches one dW tile's K (= Cpad).
-    if (chunk == 0)
-      S = choose_dh_splits(kpad, Cpad, L.Npad, (int64_t)n_dh_mt * n_nt, (int64_t)vtiles * n_nt, Cf::BK);
-    int64_t ks_len = rup(cdiv(kpad, S), Cf::BK);
-    const int S_eff = (int)cdiv(kpad, ks_len);  // non-empty splits; a later chunk has ks_len >= kpad / S, so S_eff <= S
-    if (chunk == 0) S = S_eff;
-    const int n_dh = n_dh_mt * n_nt * S_eff;
-    const int n_dw = vtiles * n_nt;
-    const int per_xcd = (int)(cdiv(n_dh, 8) + cdiv(n_dw, 8));
-    const int dh_first = ks_len >= Cpad ? 1 : 0;
-    LCE_LAUNCH("k_grad", (k_grad<T>), per_xcd * 8, kThreads, grad_lds_bytes<T>(), s, Gc, ldg, kpad, Hc,
-               W, Cpad, (int)D, (int)v0, vc, (int)(V - v0), n_nt, n_dh_mt, (int)ks_len, n_dh, vtiles,
-               dh_first, slots, slot_stride, chunk == 0 ? 0 : 1, dW, (const uint8_t*)flags, fstride,
-               filter_which);
+    if (c == 0)
+      S = choose_dh_splits(k.kpad, Cpad, L.Rpad, (int64_t)n_dh_mt * n_nt, (int64_t)k.vtiles * n_nt, Cf::BK);
+    const int64_t ks_len = rup(cdiv(k.kpad, S), Cf::BK);
+    const int S_eff = (int)cdiv(k.kpad, ks_len);  // non-empty splits; a later chunk has ks_len >= kpad / S, so S_eff <= S
+    if (c == 0) S = S_eff;
+    GradArgs<T> g;
+    g.Gc = gbuf(c);
+    g.ldg = ldg;
+    g.kpad_g = k.kpad;
+    g.Hc = Hc;
+    g.W = W;
+    g.Cpad = Cpad;
+    g.D = (int)D;
+    g.v0 = (int)k.v0;
+    g.vc = k.vc;
+    g.w_rows = (int)(V - k.v0);
+    g.n_nt = n_nt;
+    g.n_dh_mt = n_dh_mt;
+    g.ks_len = (int)ks_len;
+    g.n_dh = n_dh_mt * n_nt * S_eff;
+    g.n_dw_mt = k.vtiles;
+    g.dh_first = ks_len >= Cpad ? 1 : 0;
+    g.slots = slots;
+    g.slot_stride = slot_stride;
+    g.accumulate = c == 0 ? 0 : 1;
+    g.dW = dW;
+    g.flags = filter ? fbuf(c) : nullptr;
+    g.fstride = fstride;
+    g.fmask = filter_which;
+    const int n_dw = k.vtiles * n_nt;
+    const int n_grad = (int)(cdiv(g.n_dh, 8) + cdiv(n_dw, 8)) * 8;
+    const double gfl = 4.0 * (double)C * (double)k.vc * (double)D;  // dH and dW products of the chunk
+    if constexpr (kFuse) {
+      if (c + 1 < chunks.size()) {
+        const ReplayArgs<T> r = rargs(c + 1);
+        const int grid = n_grad + r.per_xcd * 8;
+        const double fl = gfl + replay_flops(c + 1);
+#define LCE_FUSED(FILT, BIAS)                                                                         \
+  do {                                                                                                \
+    set_lds_attr<T>((const void*)k_grad_replay<T, FILT, BIAS>, grad_replay_lds_bytes<T, FILT>());     \
+    LCE_LAUNCH_F("k_grad_replay", fl, (k_grad_replay<T, FILT, BIAS>), grid, kThreads,                 \
+                 (grad_replay_lds_bytes<T, FILT>()), s, g, r, n_grad);                                \
+  } while (0)
+        if (filter && bias_terms) LCE_FUSED(true, true);
+        else if (filter) LCE_FUSED(true, false);
+        else if (bias_terms) LCE_FUSED(false, true);
+        else LCE_FUSED(false, false);
+#undef LCE_FUSED
+        continue;
+      }
+    }
+    LCE_LAUNCH_F("k_grad", gfl, (k_grad<T>), n_grad, kThreads, grad_lds_bytes<T>(), s, g);
   }
   {
     const int64_t vec = N * (D / 4);
@@ -513,7 +621,7 @@ lce_status_t backward_entry(const void* H, const void* W, const void* b, const i
       return LCE_ERR_ARG;
     LCE_TRY(shape_supported(N, D, V, dt));
     Layout L;
-    if (!make_layout(N, D, V, dt, L)) return LCE_ERR_ARG;
+    if (!make_layout(N, D, V, dt, L, C)) return LCE_ERR_ARG;
     if (ws_bytes < L.total) return LCE_ERR_WORKSPACE;
     char* w = static_cast<char*>(ws);
     if (dt == LCE_DTYPE_BF16)
@@ -564,6 +672,12 @@ extern "C" {
 size_t lce_workspace_size(int64_t N, int64_t D, int64_t V, lce_dtype_t dt) {
   Layout L;
   if (!make_layout(N, D, V, dt, L)) return 0;
+  return L.total;
+}
+
+size_t lce_backward_workspace_size(int64_t N, int64_t C, int64_t D, int64_t V, lce_dtype_t dt) {
+  Layout L;
+  if (C < 0 || !make_layout(N, D, V, dt, L, C)) return 0;
   return L.total;
 }
 
@@ -787,10 +901,12 @@ lce_status_t lce_profile_start(int32_t max_launches) {
         if (hipEventCreate(&e) != hipSuccess) return LCE_ERR_HIP;
     }
     p.kid.assign((size_t)max_launches, -1);
+    p.lflops.assign((size_t)max_launches, 0.0);
     p.max = max_launches;
     p.used = 0;
     p.names.clear();
     p.ms.clear();
+    p.flops.clear();
     p.cnt.clear();
     p.on = true;
     return LCE_OK;
@@ -807,6 +923,7 @@ lce_status_t lce_profile_stop(void) {
     if (hipEventSynchronize(p.ev[2 * i + 1]) != hipSuccess) return LCE_ERR_HIP;
     if (hipEventElapsedTime(&ms, p.ev[2 * i], p.ev[2 * i + 1]) != hipSuccess) return LCE_ERR_HIP;
     p.ms[p.kid[i]] += ms;
+    p.flops[p.kid[i]] += p.lflops[i];
     p.cnt[p.kid[i]] += 1;
   }
   p.used = 0;
@@ -816,7 +933,7 @@ lce_status_t lce_profile_stop(void) {
 int32_t lce_profile_count(void) { return (int32_t)g_prof.names.size(); }
 
 lce_status_t lce_profile_entry(int32_t i, char* name, int32_t name_cap, double* total_ms,
-                               int64_t* launches) {
+                               int64_t* launches, double* flops) {
   Prof& p = g_prof;
   if (i < 0 || i >= (int32_t)p.names.size()) return LCE_ERR_ARG;
   if (name && name_cap > 0) {
@@ -825,6 +942,7 @@ lce_status_t lce_profile_entry(int32_t i, char* name, int32_t name_cap, double* 
   }
   if (total_ms) *total_ms = p.ms[i];
   if (launches) *launches = p.cnt[i];
+  if (flops) *flops = p.flops[i];
   return LCE_OK;
 }
 

@@ -771,14 +771,36 @@ __device__ __forceinline__ void replay_epilogue(f32x16_t (&acc)[Geo<T>::TM][Geo<
   }
 }
 
+// Arguments of one replay launch over one vocabulary chunk (see replay_body).
+template <typename T>
+struct ReplayArgs {
+  const T* W;
+  const T* bias;
+  const T* Hc;
+  const int* yc;
+  const float* mc;
+  const float* lsc;
+  const float* rsc;
+  int Cpad, D, V, v0, vtiles, tpw, n_rb, n_work, per_xcd;
+  T* Gc;
+  int64_t ldg;
+  float* dbp;
+  int64_t lddb;
+  uint8_t* flags;
+  int64_t fstride;
+  float eps;
+  int zero_dead;
+};
+
+// One workgroup's share of a replay launch; bid = its block index within the launch.
 template <typename T, bool FILTER, bool HAS_BIAS>
-__global__ __launch_bounds__(kThreads) void k_replay(
-    const T* __restrict__ W, const T* __restrict__ bias_arg, const T* __restrict__ Hc,
+__device__ __forceinline__ void replay_body(
+    int bid, const T* __restrict__ W, const T* __restrict__ bias_arg, const T* __restrict__ Hc,
     const int* __restrict__ yc, const float* __restrict__ mc, const float* __restrict__ lsc,
     const float* __restrict__ rsc, int Cpad,
     int D, int V, int v0, int vtiles, int tpw, int n_rb, int n_work, int per_xcd, T* __restrict__ Gc,
-    int64_t ldg, float* __restrict__ dbp_arg, int64_t lddb, uint8_t* __restrict__ flags = nullptr,
-    int64_t fstride = 0, float eps = 0.f, int zero_dead = 0) {
+    int64_t ldg, float* __restrict__ dbp_arg, int64_t lddb, uint8_t* __restrict__ flags,
+    int64_t fstride, float eps, int zero_dead) {
   using C = Cfg<T>;
   using G = Geo<T>;
   extern __shared__ __align__(16) char smem_raw[];
@@ -786,7 +808,7 @@ __global__ __launch_bounds__(kThreads) void k_replay(
   // absent); without it the instantiation carries neither through the loop.
   const T* __restrict__ bias = HAS_BIAS ? bias_arg : nullptr;
   float* __restrict__ dbp = HAS_BIAS ? dbp_arg : nullptr;
-  const int w = xcd_remap(blockIdx.x, per_xcd);
+  const int w = xcd_remap(bid, per_xcd);
   if (w >= n_work) return;
   int rb, vg;
   grouped_index<kGroupRows>(w, n_rb, n_work / n_rb, rb, vg);
@@ -839,6 +861,18 @@ __global__ __launch_bounds__(kThreads) void k_replay(
       __syncthreads();  // the next tile's loads reuse the LDS the db sums used
     }
   }
+}
+
+template <typename T, bool FILTER, bool HAS_BIAS>
+__device__ __forceinline__ void replay_body(int bid, const ReplayArgs<T>& a) {
+  replay_body<T, FILTER, HAS_BIAS>(bid, a.W, a.bias, a.Hc, a.yc, a.mc, a.lsc, a.rsc, a.Cpad, a.D, a.V, a.v0,
+                                   a.vtiles, a.tpw, a.n_rb, a.n_work, a.per_xcd, a.Gc, a.ldg, a.dbp, a.lddb,
+                                   a.flags, a.fstride, a.eps, a.zero_dead);
+}
+
+template <typename T, bool FILTER, bool HAS_BIAS>
+__global__ __launch_bounds__(kThreads) void k_replay(ReplayArgs<T> a) {
+  replay_body<T, FILTER, HAS_BIAS>((int)blockIdx.x, a);
 }
 
 // Stage lists of the gradient filter live in LDS after the pipeline's bytes.
@@ -928,13 +962,32 @@ __device__ __forceinline__ void grad_store(const f32x16_t (&acc)[Geo<T>::TM][Geo
   }
 }
 
+// Arguments of one gradient launch over one vocabulary chunk (see grad_body).
 template <typename T>
-__global__ __launch_bounds__(kThreads) void k_grad(
-    const T* __restrict__ Gc, int64_t ldg, int kpad_g, const T* __restrict__ Hc,
+struct GradArgs {
+  const T* Gc;
+  int64_t ldg;
+  int kpad_g;
+  const T* Hc;
+  const T* W;
+  int Cpad, D, v0, vc, w_rows, n_nt, n_dh_mt, ks_len, n_dh, n_dw_mt, dh_first;
+  float* slots;
+  int64_t slot_stride;
+  int accumulate;
+  T* dW;
+  const uint8_t* flags;
+  int64_t fstride;
+  int fmask;
+};
+
+// One workgroup's share of a gradient launch; bid = its block index within
+// the launch (its low 3 bits name the XCD the block runs on).
+template <typename T>
+__device__ __forceinline__ void grad_body(
+    int bid, const T* __restrict__ Gc, int64_t ldg, int kpad_g, const T* __restrict__ Hc,
     const T* __restrict__ W, int Cpad, int D, int v0, int vc, int w_rows, int n_nt, int n_dh_mt, int ks_len,
     int n_dh, int n_dw_mt, int dh_first, float* __restrict__ slots, int64_t slot_stride,
-    int accumulate, T* __restrict__ dW, const uint8_t* __restrict__ flags = nullptr, int64_t fstride = 0,
-    int fmask = 0) {
+    int accumulate, T* __restrict__ dW, const uint8_t* __restrict__ flags, int64_t fstride, int fmask) {
   using C = Cfg<T>;
   using G = Geo<T>;
   extern __shared__ __align__(16) char smem_raw[];
@@ -946,7 +999,7 @@ __global__ __launch_bounds__(kThreads) void k_grad(
   const int n_dw = n_dw_mt * n_nt;
   int b;
   {
-    const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
+    const int x = bid & 7, j = bid >> 3;
     const int dh_lo = (int)((int64_t)x * n_dh / 8), dh_cnt = (int)((int64_t)(x + 1) * n_dh / 8) - dh_lo;
     const int dw_lo = (int)((int64_t)x * n_dw / 8), dw_cnt = (int)((int64_t)(x + 1) * n_dw / 8) - dw_lo;
     if (dh_first)
@@ -1049,6 +1102,32 @@ __global__ __launch_bounds__(kThreads) void k_grad(
     }
     grad_store<T>(acc, dh, m0, n0, D, vc, v0, slot, accumulate, dW);
   }
+}
+
+template <typename T>
+__device__ __forceinline__ void grad_body(int bid, const GradArgs<T>& a) {
+  grad_body<T>(bid, a.Gc, a.ldg, a.kpad_g, a.Hc, a.W, a.Cpad, a.D, a.v0, a.vc, a.w_rows, a.n_nt, a.n_dh_mt,
+               a.ks_len, a.n_dh, a.n_dw_mt, a.dh_first, a.slots, a.slot_stride, a.accumulate, a.dW, a.flags,
+               a.fstride, a.fmask);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_grad(GradArgs<T> a) {
+  grad_body<T>((int)blockIdx.x, a);
+}
+
+// K5 of chunk c and K4 of chunk c+1 in one launch: blocks [0, n_grad) run the
+// gradient tiles of chunk c, which read one G buffer; the blocks after them
+// replay chunk c+1 into the other buffer.  Blocks start in index order, so
+// the replay tiles fill the CUs that the gradient tiles' last wave leaves
+// free.  n_grad is a multiple of 8, so both parts keep their XCD mapping.
+template <typename T, bool FILTER, bool HAS_BIAS>
+__global__ __launch_bounds__(kThreads) void k_grad_replay(GradArgs<T> g, ReplayArgs<T> r, int n_grad) {
+  if ((int)blockIdx.x < n_grad) grad_body<T>((int)blockIdx.x, g);
+  else replay_body<T, FILTER, HAS_BIAS>((int)blockIdx.x - n_grad, r);
+}
+template <typename T, bool FILTER> constexpr int grad_replay_lds_bytes() {
+  return grad_lds_bytes<T>() > replay_lds_bytes<T, FILTER>() ? grad_lds_bytes<T>() : replay_lds_bytes<T, FILTER>();
 }
 
 // ============================================================== K6 finalize

@@ -127,7 +127,9 @@ class LinearCrossEntropyFunction(torch.autograd.Function):
         dW = torch.empty_like(W)
         db = torch.empty_like(b) if ctx.has_bias else None
         g = grad.reshape(-1).to(torch.float32).contiguous()
-        ws = torch.empty(_lib.lce_workspace_size(N, D, V, H.dtype), dtype=torch.uint8, device=H.device)
+        # Sized for the C supervised rows (the backward's arrays take C rows).
+        ws = torch.empty(_lib.lce_backward_workspace_size(N, s.C, D, V, H.dtype), dtype=torch.uint8,
+                         device=H.device)
         if ctx.filter_eps is None:
             st = _lib.lce_backward_ex(H, W, b, labels, s.valid_idx, s.C, ctx.red, ctx.w, ctx.num, s.m, s.logs,
                                       g, dH, dW, db, ws)

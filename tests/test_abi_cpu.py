@@ -61,6 +61,26 @@ def test_workspace_size_never_scales_with_N_times_V(lib):
     assert lib.lce_workspace_size(64, 128, 1000, F32) > 0
 
 
+def test_backward_workspace_scales_with_the_supervised_rows(lib):
+    """lce_backward_workspace_size(N, C, ...) is the worst-case size at C = N,
+    never more, shrinks with C by at least the two bf16 chunks of the gradient
+    tile store (2 x 32768 entries per 256 rows dropped), and refuses C outside [0, N]."""
+    BF16, F32 = _lib.LCE_DTYPE_BF16, _lib.LCE_DTYPE_F32
+    N, D, V = 16384, 1024, 248320
+    full = lib.lce_workspace_size(N, D, V, BF16)
+    assert lib.lce_backward_workspace_size(N, N, D, V, BF16) == full
+    prev = full
+    for C in (16000, 11471, 4096, 256, 1, 0):
+        ws = lib.lce_backward_workspace_size(N, C, D, V, BF16)
+        assert 0 < ws <= prev, (C, ws, prev)
+        dropped_rows = (N - max(-(-C // 256) * 256, 256))
+        assert full - ws >= dropped_rows * 2 * 32768 * 2, (C, full - ws)
+        prev = ws
+    assert lib.lce_backward_workspace_size(N, N + 1, D, V, BF16) == 0
+    assert lib.lce_backward_workspace_size(N, -1, D, V, BF16) == 0
+    assert lib.lce_backward_workspace_size(64, 10, 128, 1000, F32) <= lib.lce_workspace_size(64, 128, 1000, F32)
+
+
 def test_host_argument_checks_return_before_any_hip_call(lib):
     C = ctypes.c_int64(5)
     # null C_host / negative N / bad V
