@@ -227,7 +227,13 @@ def main():
     torch.cuda.synchronize()
     base_alloc = torch.cuda.memory_allocated()
     torch.cuda.reset_peak_memory_stats()
-    ws = torch.empty(_lib.lce_workspace_size(N, D, V, H.dtype), dtype=torch.uint8, device=dev)
+    # The backward's arrays take the supervised rows only: size the one
+    # workspace that every call of the step shares for this workload's count.
+    sup = wl.labels != wl.ignore_index
+    if wl.mask is not None:
+        sup &= wl.mask.bool()
+    ws = torch.empty(_lib.lce_backward_workspace_size(N, int(sup.sum()), D, V, H.dtype), dtype=torch.uint8,
+                     device=dev)
     idx = torch.empty(N, dtype=torch.int32, device=dev)
     loss = torch.empty(1, dtype=torch.float32, device=dev)
     m = torch.empty(N, dtype=torch.float32, device=dev)
