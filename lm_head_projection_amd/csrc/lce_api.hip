@@ -427,7 +427,10 @@ lce_status_t backward_impl(const T* H, const T* W, const T* b, const int64_t* la
     a.V = (int)V;
     a.v0 = (int)k.v0;
     a.vtiles = k.vtiles;
-    a.tpw = choose_tiles_per_wg(n_rb, k.vtiles, (int)cdiv(D, sizeof(T) == 2 ? 64 : Cf::BK));
+    // Inside a fused launch (chunks 1...) the replay items fill the CUs the
+    // gradient items leave: short items of 2 tiles pack that tail best.
+    a.tpw = kFuse && c > 0 ? std::min(2, k.vtiles)
+                           : choose_tiles_per_wg(n_rb, k.vtiles, (int)cdiv(D, sizeof(T) == 2 ? 64 : Cf::BK));
     a.n_rb = n_rb;
     a.n_work = n_rb * (int)cdiv(k.vtiles, a.tpw);
     a.per_xcd = (int)cdiv(a.n_work, 8);

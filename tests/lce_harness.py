@@ -16,6 +16,7 @@ from typing import Optional
 import numpy as np
 import torch
 
+import oracle as O
 from lm_head_projection_amd import _lib
 from lm_head_projection_amd.workloads import Workload
 
@@ -52,8 +53,10 @@ def to_np(t):
 
 
 def run_gpu(wl: Workload, lam: float = 1.0, backward: bool = True, grad_ptr: bool = True,
-            dev: str = "cuda:0", keep_device: bool = False):
-    """compact -> forward -> backward through the C ABI; results on the host."""
+            dev: str = "cuda:0", keep_device: bool = False, exact_ws: bool = False):
+    """compact -> forward -> backward through the C ABI; results on the host.
+    exact_ws: one workspace of exactly lce_backward_workspace_size(N, C, ...)
+    bytes for the workload's supervised count C (else the worst case C = N)."""
     H = wl.H.to(dev)
     W = wl.W.to(dev)
     b = None if wl.b is None else wl.b.to(dev)
@@ -61,7 +64,14 @@ def run_gpu(wl: Workload, lam: float = 1.0, backward: bool = True, grad_ptr: boo
     mask = None if wl.mask is None else wl.mask.to(torch.uint8).to(dev)
     N, D = H.shape
     V = W.shape[0]
-    ws = torch.empty(_lib.lce_workspace_size(N, D, V, H.dtype), dtype=torch.uint8, device=dev)
+    if exact_ws:
+        sup = wl.labels != wl.ignore_index
+        if wl.mask is not None:
+            sup &= wl.mask.bool()
+        nbytes = _lib.lce_backward_workspace_size(N, int(sup.sum()), D, V, H.dtype)
+    else:
+        nbytes = _lib.lce_workspace_size(N, D, V, H.dtype)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     idx = torch.full((max(N, 1),), -7, dtype=torch.int32, device=dev)
     st_c, C = _lib.lce_compact_valid(labels, mask, V, wl.ignore_index, idx, ws)
     loss = torch.full((1,), float("nan"), dtype=torch.float32, device=dev)
@@ -193,3 +203,34 @@ def run_gpu_filtered(wl: Workload, eps: float, reduction: str = "mean", weights=
                                     dH, dW, db, ws, which=which)
     torch.cuda.synchronize()
     return st, to_np(dH), to_np(dW), to_np(db)
+
+
+def oracle_of(wl, lam=1.0):
+    """The oracle's dense forward and backward of a workload (float64)."""
+    H, W = wl.H.double().numpy(), wl.W.double().numpy()
+    b = None if wl.b is None else wl.b.double().numpy()
+    mask = None if wl.mask is None else wl.mask.numpy()
+    return O.dense_forward_backward(H, W, b, wl.labels.numpy(), mask, lam, wl.ignore_index)
+
+
+def check_all(wl, r, f, g, dtype):
+    """Every output of run_gpu against the oracle (f, g) at the stated tolerances."""
+    t = tol(dtype)
+    assert r.status_c == _lib.LCE_OK, r.status_c
+    assert r.C == f.C
+    np.testing.assert_array_equal(r.idx, f.idx)
+    assert r.status_f == _lib.LCE_OK
+    assert abs(r.loss - f.loss) <= t["loss"] * abs(f.loss), (r.loss, f.loss)
+    a = np.zeros(wl.N, dtype=bool)
+    a[f.idx] = True
+    assert_stat_close("m", r.m[a], f.m[a], t["stat"])
+    assert_stat_close("logs", r.logs[a], f.logs[a], t["stat"])
+    assert_stat_close("row_loss", r.row_loss[a], f.row_loss[a], t["stat"])
+    assert np.all(np.isneginf(r.m[~a])) and np.all(np.isneginf(r.logs[~a]))
+    assert np.all(r.row_loss[~a] == 0.0)
+    assert r.status_b == _lib.LCE_OK
+    assert_grad_close("dH", r.dH, g.dH, t["grad"])
+    assert np.all(r.dH[~a] == 0.0), "unsupervised dH rows must be exactly 0"
+    assert_grad_close("dW", r.dW, g.dW, t["grad"])
+    if wl.b is not None:
+        assert_grad_close("db", r.db, g.db, t["grad"])

@@ -81,6 +81,22 @@ def test_backward_workspace_scales_with_the_supervised_rows(lib):
     assert lib.lce_backward_workspace_size(64, 10, 128, 1000, F32) <= lib.lce_workspace_size(64, 128, 1000, F32)
 
 
+def test_backward_refuses_a_workspace_below_its_size_before_any_hip_call(lib):
+    """lce_backward with C supervised rows needs lce_backward_workspace_size(N, C,
+    ...) bytes: one byte less is LCE_ERR_WORKSPACE, decided on the host (the
+    device pointers here are never dereferenced)."""
+    BF16 = _lib.LCE_DTYPE_BF16
+    N, C, D, V = 300, 100, 128, 70000
+    need = lib.lce_backward_workspace_size(N, C, D, V, BF16)
+    assert 0 < need < lib.lce_workspace_size(N, D, V, BF16)
+    p = ctypes.c_void_p(1 << 20)  # 16-byte aligned stand-in
+    st = lib.lce_backward(p, p, None, p, p, C, N, D, V, BF16, p, p, None, p, p, None, p, need - 1, None)
+    assert st == _lib.LCE_ERR_WORKSPACE
+    # C is bounded by N before the size is looked at
+    st = lib.lce_backward(p, p, None, p, p, N + 1, N, D, V, BF16, p, p, None, p, p, None, p, need, None)
+    assert st == _lib.LCE_ERR_ARG
+
+
 def test_host_argument_checks_return_before_any_hip_call(lib):
     C = ctypes.c_int64(5)
     # null C_host / negative N / bad V

@@ -15,38 +15,9 @@ import oracle as O
 from lm_head_projection_amd import _lib
 from lm_head_projection_amd import workloads as WL
 
-from lce_harness import (assert_grad_close, assert_stat_close, run_gpu, say, tol)
+from lce_harness import (assert_grad_close, assert_stat_close, check_all, oracle_of, run_gpu, say, tol)
 
 pytestmark = pytest.mark.gpu
-
-
-def oracle_of(wl, lam=1.0):
-    H, W = wl.H.double().numpy(), wl.W.double().numpy()
-    b = None if wl.b is None else wl.b.double().numpy()
-    mask = None if wl.mask is None else wl.mask.numpy()
-    return O.dense_forward_backward(H, W, b, wl.labels.numpy(), mask, lam, wl.ignore_index)
-
-
-def check_all(wl, r, f, g, dtype):
-    t = tol(dtype)
-    assert r.status_c == _lib.LCE_OK, r.status_c
-    assert r.C == f.C
-    np.testing.assert_array_equal(r.idx, f.idx)
-    assert r.status_f == _lib.LCE_OK
-    assert abs(r.loss - f.loss) <= t["loss"] * abs(f.loss), (r.loss, f.loss)
-    a = np.zeros(wl.N, dtype=bool)
-    a[f.idx] = True
-    assert_stat_close("m", r.m[a], f.m[a], t["stat"])
-    assert_stat_close("logs", r.logs[a], f.logs[a], t["stat"])
-    assert_stat_close("row_loss", r.row_loss[a], f.row_loss[a], t["stat"])
-    assert np.all(np.isneginf(r.m[~a])) and np.all(np.isneginf(r.logs[~a]))
-    assert np.all(r.row_loss[~a] == 0.0)
-    assert r.status_b == _lib.LCE_OK
-    assert_grad_close("dH", r.dH, g.dH, t["grad"])
-    assert np.all(r.dH[~a] == 0.0), "unsupervised dH rows must be exactly 0"
-    assert_grad_close("dW", r.dW, g.dW, t["grad"])
-    if wl.b is not None:
-        assert_grad_close("db", r.db, g.db, t["grad"])
 
 
 @pytest.mark.parametrize("name", WL.SMALL_CONFIGS)
