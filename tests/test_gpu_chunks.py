@@ -127,3 +127,23 @@ def test_three_chunks_filter_without_bias():
     t = tol(wl.dtype)
     assert_grad_close("dH", dH, gf.dH, t["grad"])
     assert_grad_close("dW", dW, gf.dW, t["grad"])
+
+
+@pytest.mark.parametrize("V", [32768, 32769, 65536])
+def test_chunk_boundaries(V):
+    """One whole chunk (no fused launch), one chunk plus a single entry (the
+    fused launch replays a 1-entry chunk of one ragged tile), and two whole
+    chunks, with a bias."""
+    wl = WL.make_random(300, 64, V, dtype=torch.bfloat16, seed=71, ignore_frac=0.2)
+    say(f"[chunks] boundary V={V}")
+    f, g = oracle_of(wl)
+    r = run_gpu(wl)
+    check_all(wl, r, f, g, wl.dtype)
+
+
+def test_fp32_several_chunks():
+    """fp32 keeps separate replay and gradient launches over one G buffer."""
+    wl = WL.make_random(200, 64, 40000, dtype=torch.float32, seed=73, ignore_frac=0.2)
+    f, g = oracle_of(wl)
+    r = run_gpu(wl)
+    check_all(wl, r, f, g, wl.dtype)
