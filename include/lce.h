@@ -25,8 +25,11 @@
  *    with fp32 accumulation, the scores Z and every statistic are fp32.
  *  - D must be a multiple of 8 (bf16) or 4 (fp32).
  *  - The caller owns all memory, including the workspace (size it with
- *    lce_workspace_size, or lce_forward_workspace_size for the compaction
- *    and forward calls alone).  The library never allocates device memory.  Its
+ *    lce_workspace_size for every call, lce_forward_workspace_size for the
+ *    compaction and forward calls alone, or lce_backward_workspace_size for
+ *    the backward calls once C is known).  A call given fewer bytes than it
+ *    needs returns LCE_ERR_WORKSPACE before any HIP call.  The library never
+ *    allocates device memory.  Its
  *    only state between calls is a per-device record of the kernel
  *    attributes it has set and the optional profiling switch at the end of
  *    this header.  Inputs are never written.
@@ -100,8 +103,8 @@ size_t lce_backward_workspace_size(int64_t N, int64_t C, int64_t D, int64_t V, l
  * (lce_compact_valid, lce_forward, lce_forward_ex, lce_forward_shard with the
  * shard's V): the gathered supervised rows and the per-split row partials,
  * about N x D elements plus 0.5 KB per position.  A caller can free this
- * buffer after the forward call and allocate the lce_workspace_size buffer
- * only for the backward call, so that nothing beyond m and logs (the two
+ * buffer after the forward call and allocate the lce_backward_workspace_size
+ * buffer only for the backward call, so that nothing beyond m and logs (the two
  * N-vectors that section 02 of the glenzli.com page saves) is held between
  * the passes.  Returns 0 for invalid sizes; never more than
  * lce_workspace_size. */
@@ -150,7 +153,9 @@ lce_status_t lce_forward(const void* H, const void* W, const void* b, const int6
  * Deterministic: the same inputs give bitwise-identical outputs (ordered
  * reductions; the only floating-point atomics add into partial sums that
  * have one writer per kernel launch, with launches in a fixed order).
- * C == 0: dH, dW and db are zero-filled, returns LCE_OK_EMPTY. */
+ * C == 0: dH, dW and db are zero-filled, returns LCE_OK_EMPTY.
+ *   ws: at least lce_backward_workspace_size(N, C, D, V, dt) bytes (the
+ *   lce_workspace_size buffer of the forward call also serves). */
 lce_status_t lce_backward(const void* H, const void* W, const void* b, const int64_t* labels,
                           const int32_t* valid_idx, int64_t C, int64_t N, int64_t D, int64_t V,
                           lce_dtype_t dt, const float* m, const float* logs,
