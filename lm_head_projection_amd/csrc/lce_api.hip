@@ -204,7 +204,7 @@ int choose_split(int n_rb, int n_vt) {
   return best;
 }
 
-// Makespan of k_grad's schedule: each of the 8 XCDs takes an equal share of
+// Makespan of a chunk's gradient items: each of the 8 XCDs takes an equal share of
 // the n_a items of length L_a and of the n_b items of length L_b, and runs its
 // share on its kCUs/8 workgroup slots, the longer kind first, each item on the
 // slot that frees first (the dispatcher's order).

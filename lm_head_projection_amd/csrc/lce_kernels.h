@@ -4,8 +4,11 @@
 //   K1  k_gather                                   supervised rows H[idx] -> Hc
 //   K2  k_fwd                                      score tiles + running (m, s)
 //   K3  k_merge / k_loss_sum                       split merge, per-row CE, mean
-//   K4  k_replay                                   score tiles -> G = p - onehot
-//   K5  k_grad                                     dH (+= G W) and dW (= G^T Hc)
+//   K4  replay_body                                score tiles -> G = p - onehot
+//   K5  grad_body                                  dH (+= G W) and dW (= G^T Hc)
+//       launched as k_replay (K4 of the first chunk), k_grad_replay (K5 of
+//       chunk c with K4 of chunk c+1, bf16) and k_grad (K5 of the last chunk;
+//       fp32: K4 and K5 of every chunk apart)
 //   K6  k_dh_finalize / k_db_finalize              ordered sums, cast
 //   k_row_scale                                    per-row factor r_c of G
 //
@@ -561,7 +564,7 @@ __global__ void k_store_scalar(float* __restrict__ p, float v) { p[0] = v; }
 // buffer, and, with a bias, the per-row-block column sums of G (db partials)
 // in a fixed order.
 // FILTER: also mark, per block of 256 rows x 32 vocabulary entries of G, whether
-// the block is live for the gradient GEMMs (see k_grad): some entry with
+// the block is live for the gradient GEMMs (see grad_body): some entry with
 // |r| p >= eps |r| (r != 0), or the block holds a row's target column.
 template <typename T, bool FILTER = false>
 __device__ __forceinline__ void replay_epilogue(f32x16_t (&acc)[Geo<T>::TM][Geo<T>::TN],
@@ -880,11 +883,13 @@ __global__ __launch_bounds__(kThreads) void k_replay(ReplayArgs<T> a) {
 // Stage lists of the gradient filter live in LDS after the pipeline's bytes.
 constexpr int kFilterListCap = 3584;  // entries (14 KB) + 8 wave sums
 constexpr int kFilterLdsBytes = (kFilterListCap + 8) * 4;
-// k_grad's dynamic LDS: the BK=32 pipeline, plus the filter's stage list (bf16).
+// The gradient items' dynamic LDS: the BK=32 ring (the BK=64 core fits in it),
+// plus the filter's stage list (bf16).
 template <typename T> constexpr int grad_lds_bytes() {
   return sizeof(T) == 2 ? pipe32::LDS_BYTES + kFilterLdsBytes : Geo<T>::LDS_BYTES;
 }
 static_assert(pipe32::LDS_BYTES + kFilterLdsBytes <= 160 * 1024, "LDS of one workgroup per CU");
+static_assert(pipe::RING_BYTES <= pipe32::LDS_BYTES, "the BK=64 gradient core uses the same LDS");
 
 // Compacts {i < n : live(i)} in ascending order into list, each i expanded
 // to `expand` consecutive stages i*expand + 0..expand-1; returns the number
