@@ -36,10 +36,10 @@ static_assert(Geo<uint16_t>::TM == pipe32::TM && Geo<uint16_t>::TN == pipe32::TN
 // a_i = 1[mask_i] 1[y_i != ignore] (section 01).  Three passes: per-block
 // counts, one-block exclusive scan of the counts, ordered scatter.  No atomics.
 constexpr int kCmpBlock = 256;
-// Row blocks per L2 group in the score-tile kernels (see grouped_index): the
-// forward walks each item's W tiles with a fixed block of rows, so its groups
-// are smaller (4 row blocks keep an XCD's H_c share at 2 MB of its 4 MB L2).
-constexpr int kGroupRows = 8, kGroupRowsFwd = 4;
+// Row blocks per L2 group in the score-tile kernels (see grouped_index): each
+// item walks its W tiles with a fixed block of rows, and 4 row blocks keep an
+// XCD's share of H_c at 2 MB of its 4 MB L2.
+constexpr int kGroupRows = 4;
 
 __device__ __forceinline__ bool is_supervised(const int64_t* labels, const uint8_t* mask, int64_t i,
                                               int64_t ignore) {
@@ -329,7 +329,7 @@ __global__ __launch_bounds__(kThreads) void k_fwd(const T* __restrict__ W, const
   const int w = xcd_remap(blockIdx.x, per_xcd);
   if (w >= n_work) return;
   int rb, split;
-  grouped_index<kGroupRowsFwd>(w, n_rb, n_split, rb, split);
+  grouped_index<kGroupRows>(w, n_rb, n_split, rb, split);
   const int t0 = (int)((int64_t)split * n_vt / n_split);
   const int t1 = (int)((int64_t)(split + 1) * n_vt / n_split);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
