@@ -29,6 +29,10 @@ constexpr int kMaxSplit = 64;         // vocabulary splits of the forward pass
 constexpr int kDhSlotRows = 4;        // the dH slots hold 4 x Rpad rows of D fp32 values
 constexpr int kMaxDhSlots = 16;       // k-splits of the dH GEMM (at most)
 constexpr int kCUs = 256;             // MI355X compute units (one 512-thread workgroup each)
+// Replay tiles per CU below which a fused launch's replay items take one tile
+// each instead of two (measured: 2.5 and 14.5 tiles per CU gain with single
+// tiles, 22.5 lose).
+constexpr int kFusedTilesPerCu = 16;
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t rup(int64_t a, int64_t b) { return cdiv(a, b) * b; }
@@ -428,8 +432,9 @@ lce_status_t backward_impl(const T* H, const T* W, const T* b, const int64_t* la
     a.v0 = (int)k.v0;
     a.vtiles = k.vtiles;
     // Inside a fused launch (chunks 1...) the replay items fill the CUs the
-    // gradient items leave: short items of 2 tiles pack that tail best.
-    a.tpw = kFuse && c > 0 ? std::min(2, k.vtiles)
+    // gradient items leave: short items pack that tail best, 2 tiles each, or
+    // single tiles when the chunk has fewer than kFusedTilesPerCu of them per CU.
+    a.tpw = kFuse && c > 0 ? std::min((int64_t)n_rb * k.vtiles < (int64_t)kFusedTilesPerCu * kCUs ? 1 : 2, k.vtiles)
                            : choose_tiles_per_wg(n_rb, k.vtiles, (int)cdiv(D, sizeof(T) == 2 ? 64 : Cf::BK));
     a.n_rb = n_rb;
     a.n_work = n_rb * (int)cdiv(k.vtiles, a.tpw);
