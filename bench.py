@@ -39,7 +39,7 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=12)
-    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="packed")
     p.add_argument("--mode", choices=("train", "forward", "shard"), default="train",
                    help="train: compaction + forward + backward; forward: compaction + forward-only loss; "
@@ -308,18 +308,20 @@ def main():
     if args.mode != "shard":
         step = step_single
 
+    # HIP events on the stream, one between every two timed steps (per-step
+    # times for the median).  They are made before the warm-up, and the
+    # output check waits until after the timed region: host work between the
+    # warm-up and the timed steps leaves the GPU idle, and after an idle gap
+    # its clock needs one packed step (several short ones) to recover.
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     for i in range(args.warmup):
         C = step()
         log(f"[bench] warmup {i + 1}/{args.warmup} done")
-    torch.cuda.synchronize()
-    assert torch.isfinite(loss).all()
     if not train:
         log("[bench] forward-only: compaction + forward, no saved statistics")
 
-    # Timed region: K steps bracketed by synchronisation; HIP events on the
-    # stream, one between every two steps (per-step times for the median).
+    # Timed region: K steps bracketed by synchronisation.
     torch.cuda.synchronize()
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     evs[0].record(stream)
     wall0 = time.perf_counter()
     for i in range(args.steps):
@@ -329,8 +331,11 @@ def main():
     wall = time.perf_counter() - wall0
     total_ms = evs[0].elapsed_time(evs[-1])
     ms = total_ms / args.steps
-    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
-    step_ms = {"mean": ms, "median": statistics.median(per_step), "min": per_step[0], "max": per_step[-1]}
+    in_order = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
+    per_step = sorted(in_order)
+    step_ms = {"mean": ms, "median": statistics.median(per_step), "min": per_step[0], "max": per_step[-1],
+               "in_order": [round(t, 4) for t in in_order]}
+    assert torch.isfinite(loss).all()
     peak_extra = torch.cuda.max_memory_allocated() - base_alloc
     log(f"[bench] {args.steps} steps: {ms:.3f} ms/step (median {step_ms['median']:.3f}, min {step_ms['min']:.3f}, "
         f"max {step_ms['max']:.3f}; wall {wall * 1e3 / args.steps:.3f} ms/step), C={C}")
