@@ -86,13 +86,16 @@ def step_flops(C, D, V, mode="train"):
 def kernel_bytes(C, N, D, V, esz, has_mask, has_bias):
     """Algorithmic HBM bytes per launch of the memory-bound kernels: the
     compaction (labels and mask read, indices written), the row gather, and
-    the two finalisations.  k_dh_finalize reads at least one fp32 partial per
-    supervised element (more when the library splits dH over several slots),
-    so its figure is a lower bound."""
+    the two finalisations.  The gather also fills per-position arrays, 4 bytes
+    a position each: m and log s in the forward call, the inverse row map in
+    the backward call (1.5 arrays a launch on average over a training step).
+    k_dh_finalize reads at least one fp32 partial per supervised element (more
+    when the library splits dH over several slots), so its figure is a lower
+    bound."""
     cpad = -(-C // 256) * 256
     per_pos = 8 + (1 if has_mask else 0)
-    out = {"k_cmp_count": N * per_pos, "k_cmp_scatter": N * per_pos + 4 * C,
-           "k_gather": C * D * esz + cpad * D * esz,
+    out = {"k_cmp_one": N * per_pos + 4 * C, "k_cmp_count": N * per_pos, "k_cmp_scatter": N * per_pos + 4 * C,
+           "k_gather": C * D * esz + cpad * D * esz + 6 * N,
            "k_dh_finalize": C * D * 4 + N * D * esz}
     if has_bias:
         out["k_db_finalize"] = (cpad // 256) * (-(-V // 256) * 256) * 4 + V * esz

@@ -284,10 +284,11 @@ lce_status_t zero_bytes(void* p, int64_t bytes, hipStream_t s) {
   return LCE_OK;
 }
 
-lce_status_t fill_f32(float* p, int64_t n, float v, hipStream_t s) {
-  if (!p || n <= 0) return LCE_OK;
+// m = log s = -inf and l = 0 at all n positions (each array may be null).
+lce_status_t fill_stats(float* m, float* logs, float* row_loss, int64_t n, hipStream_t s) {
+  if ((!m && !logs && !row_loss) || n <= 0) return LCE_OK;
   const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(cdiv(n, 256), 4096));
-  LCE_LAUNCH("k_fill_f32", k_fill_f32, grid, 256, 0, s, p, n, v);
+  LCE_LAUNCH("k_fill_stats", k_fill_stats, grid, 256, 0, s, m, logs, row_loss, n);
   return LCE_OK;
 }
 
@@ -315,8 +316,16 @@ lce_status_t forward_impl(const T* H, const T* W, const T* b, const int64_t* lab
   {
     const int64_t vec = (int64_t)Cpad * (D / (16 / (int64_t)sizeof(T)));
     const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(cdiv(vec, 256), 8192));
+    // The vocabulary shard path writes no per-position statistics.
+    PosFill fill;
+    if (!shard_part) {
+      fill.m = m;
+      fill.logs = logs;
+      fill.row_loss = row_loss;
+      fill.N = N;
+    }
     LCE_LAUNCH("k_gather", (k_gather<T>), grid, 256, 0, s, H, labels, idx, (int)C, Cpad, (int)D, label_off, Hc,
-               yc, (const float*)nullptr, (const float*)nullptr, (float*)nullptr, (float*)nullptr);
+               yc, (const float*)nullptr, (const float*)nullptr, (float*)nullptr, (float*)nullptr, fill);
   }
   const int n_rb = Cpad / Cf::BN;
   const int n_vt = (int)cdiv(V, Cf::BM);
@@ -338,9 +347,6 @@ lce_status_t forward_impl(const T* H, const T* W, const T* b, const int64_t* lab
                (int)V, shard_part, shard_part + C, shard_part + 2 * C);
     return LCE_OK;
   }
-  LCE_TRY(fill_f32(m, N, -INFINITY, s));
-  LCE_TRY(fill_f32(logs, N, -INFINITY, s));
-  LCE_TRY(fill_f32(row_loss, N, 0.f, s));
   LCE_LAUNCH("k_merge", k_merge, cdiv(C, 256), 256, 0, s, pm, ps, tgt, n_split, Cpad, (int)C, idx, m,
              logs, row_loss, lrow);
   if (loss)
@@ -374,16 +380,14 @@ lce_status_t backward_impl(const T* H, const T* W, const T* b, const int64_t* la
   {
     const int64_t vec = (int64_t)Cpad * (D / (16 / (int64_t)sizeof(T)));
     const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(cdiv(vec, 256), 8192));
+    PosFill fill;
+    fill.inv = inv;
+    fill.N = N;
     LCE_LAUNCH("k_gather", (k_gather<T>), grid, 256, 0, s, H, labels, idx, (int)C, Cpad, (int)D, label_off, Hc,
-               yc, m, logs, mc, lsc);
+               yc, m, logs, mc, lsc, fill);
   }
-  {
-    const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(cdiv(N, 256), 4096));
-    LCE_LAUNCH("k_fill_i32", k_fill_i32, grid, 256, 0, s, inv, N, -1);
-    LCE_LAUNCH("k_inv_scatter", k_inv_scatter, cdiv(C, 256), 256, 0, s, idx, (int)C, inv);
-    LCE_LAUNCH("k_row_scale", k_row_scale, cdiv(Cpad, 256), 256, 0, s, idx, (int)C, Cpad, (int)red.kind,
-               red.weights, (float)red.div, grad_loss, rsc);
-  }
+  LCE_LAUNCH("k_row_scale", k_row_scale, cdiv(Cpad, 256), 256, 0, s, idx, (int)C, Cpad, (int)red.kind,
+             red.weights, (float)red.div, grad_loss, rsc, inv);
   const int n_rb = Cpad / Cf::BN;
   const int n_nt = (int)cdiv(D, Cf::BN);
   const int n_dh_mt = Cpad / Cf::BM;
@@ -583,9 +587,7 @@ lce_status_t forward_entry(const void* H, const void* W, const void* b, const in
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (C == 0) {
       if (loss) LCE_LAUNCH("k_store_scalar", k_store_scalar, 1, 1, 0, s, loss, 0.f);
-      LCE_TRY(fill_f32(m, N, -INFINITY, s));
-      LCE_TRY(fill_f32(logs, N, -INFINITY, s));
-      LCE_TRY(fill_f32(row_loss, N, 0.f, s));
+      LCE_TRY(fill_stats(m, logs, row_loss, N, s));
       return LCE_OK_EMPTY;
     }
     if (!H || !W || !labels || !valid_idx || !ws) return LCE_ERR_ARG;
@@ -730,11 +732,15 @@ lce_status_t lce_compact_valid(const int64_t* labels, const uint8_t* mask, int64
     int* offsets = reinterpret_cast<int*>(w + L.offsets);
     int* stat = reinterpret_cast<int*>(w + L.stat);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    LCE_LAUNCH("k_cmp_count", k_cmp_count, nblk, kCmpBlock, 0, s, labels, mask, N, V, ignore_index,
-               counts, bad);
-    LCE_LAUNCH("k_cmp_scan", k_cmp_scan, 1, 1024, 0, s, counts, bad, (int)nblk, offsets, stat);
-    LCE_LAUNCH("k_cmp_scatter", k_cmp_scatter, nblk, kCmpBlock, 0, s, labels, mask, N, ignore_index,
-               offsets, valid_idx);
+    if (N <= kCmpOneMax) {
+      LCE_LAUNCH("k_cmp_one", k_cmp_one, 1, 1024, 0, s, labels, mask, N, V, ignore_index, valid_idx, stat);
+    } else {
+      LCE_LAUNCH("k_cmp_count", k_cmp_count, nblk, kCmpBlock, 0, s, labels, mask, N, V, ignore_index,
+                 counts, bad);
+      LCE_LAUNCH("k_cmp_scan", k_cmp_scan, 1, 1024, 0, s, counts, bad, (int)nblk, offsets, stat);
+      LCE_LAUNCH("k_cmp_scatter", k_cmp_scatter, nblk, kCmpBlock, 0, s, labels, mask, N, ignore_index,
+                 offsets, valid_idx);
+    }
     int host_stat[2] = {0, 0};
     if (hipMemcpyAsync(host_stat, stat, sizeof(host_stat), hipMemcpyDeviceToHost, s) != hipSuccess)
       return LCE_ERR_HIP;
@@ -848,17 +854,13 @@ lce_status_t lce_merge_shards(const float* parts, int32_t P, const int64_t* shar
     float* row_loss = red.kind == kReduceNone ? loss : nullptr;
     if (C == 0) {
       if (red.kind != kReduceNone) LCE_LAUNCH("k_store_scalar", k_store_scalar, 1, 1, 0, s, loss, 0.f);
-      LCE_TRY(fill_f32(m, N, -INFINITY, s));
-      LCE_TRY(fill_f32(logs, N, -INFINITY, s));
-      LCE_TRY(fill_f32(row_loss, N, 0.f, s));
+      LCE_TRY(fill_stats(m, logs, row_loss, N, s));
       return LCE_OK_EMPTY;
     }
     if (!parts || !labels || !valid_idx || !ws) return LCE_ERR_ARG;
     if (ws_bytes < (size_t)C * sizeof(float)) return LCE_ERR_WORKSPACE;
     float* lrow = static_cast<float*>(ws);
-    LCE_TRY(fill_f32(m, N, -INFINITY, s));
-    LCE_TRY(fill_f32(logs, N, -INFINITY, s));
-    LCE_TRY(fill_f32(row_loss, N, 0.f, s));
+    LCE_TRY(fill_stats(m, logs, row_loss, N, s));
     LCE_LAUNCH("k_merge_shards", k_merge_shards, cdiv(C, 256), 256, 0, s, parts, parts + C, parts + 2 * C, (int)P,
                3 * C, bounds, labels, valid_idx, (int)C, m, logs, row_loss, lrow);
     if (red.kind != kReduceNone)

@@ -1,7 +1,9 @@
 // Kernels of the fused linear-cross-entropy path (gfx950).
 //
-//   K0  k_cmp_count / k_cmp_scan / k_cmp_scatter   valid-token compaction
+//   K0  k_cmp_one, or k_cmp_count / k_cmp_scan /   valid-token compaction
+//       k_cmp_scatter above 65536 positions
 //   K1  k_gather                                   supervised rows H[idx] -> Hc
+//                                                  (and per-position fills)
 //   K2  k_fwd                                      score tiles + running (m, s)
 //   K3  k_merge / k_loss_sum                       split merge, per-row CE, mean
 //   K4  replay_body                                score tiles -> G = p - onehot
@@ -10,7 +12,8 @@
 //       chunk c with K4 of chunk c+1, bf16) and k_grad (K5 of the last chunk;
 //       fp32: K4 and K5 of every chunk apart)
 //   K6  k_dh_finalize / k_db_finalize              ordered sums, cast
-//   k_row_scale                                    per-row factor r_c of G
+//   k_row_scale                                    per-row factor r_c of G,
+//                                                  inverse row map
 //
 // Page references are to "分块交叉熵：从输出投影开始省保存量" (glenzli.com):
 // section 01 (objective, tile steps), section 02 (running LSE), section 04
@@ -127,6 +130,47 @@ __global__ __launch_bounds__(1024) void k_cmp_scan(const int* __restrict__ count
   }
 }
 
+// The same compaction in one workgroup, for N <= kCmpOneMax: the block walks
+// the positions in rounds of 1024 x kCmpPer (each thread a run of kCmpPer
+// consecutive positions), scans the per-thread counts across the block and
+// writes each round's supervised positions after the previous rounds'.  One
+// launch instead of three, for the sizes where launches dominate.
+constexpr int kCmpPer = 8;
+constexpr int64_t kCmpOneMax = 65536;
+__global__ __launch_bounds__(1024) void k_cmp_one(const int64_t* __restrict__ labels,
+                                                  const uint8_t* __restrict__ mask, int64_t N, int64_t V,
+                                                  int64_t ignore, int32_t* __restrict__ idx, int* stat) {
+  __shared__ int s_w[16];
+  int carry = 0, anybad = 0;
+  for (int64_t base = 0; base < N; base += 1024 * kCmpPer) {
+    const int64_t i0 = base + (int64_t)threadIdx.x * kCmpPer;
+    uint32_t bits = 0;
+    int cnt = 0;
+    bool oob = false;
+#pragma unroll
+    for (int k = 0; k < kCmpPer; ++k) {
+      const int64_t i = i0 + k;
+      if (i < N && is_supervised(labels, mask, i, ignore)) {
+        bits |= 1u << k;
+        ++cnt;
+        const int64_t y = labels[i];
+        oob = oob || y < 0 || y >= V;
+      }
+    }
+    int total;
+    int o = carry + block_excl_scan_1024(cnt, s_w, total);
+#pragma unroll
+    for (int k = 0; k < kCmpPer; ++k)
+      if ((bits >> k) & 1u) idx[o++] = (int32_t)(i0 + k);
+    carry += total;
+    anybad |= __syncthreads_or(oob);
+  }
+  if (threadIdx.x == 0) {
+    stat[0] = carry;
+    stat[1] = anybad;
+  }
+}
+
 __global__ __launch_bounds__(kCmpBlock) void k_cmp_scatter(const int64_t* __restrict__ labels,
                                                            const uint8_t* __restrict__ mask,
                                                            int64_t N, int64_t ignore,
@@ -149,6 +193,17 @@ __global__ __launch_bounds__(kCmpBlock) void k_cmp_scatter(const int64_t* __rest
 // Hc[c] = H[idx[c]] for c < C, 0 for C <= c < Cpad; yc[c] = y[idx[c]] (-1 for
 // padding).  With m/logs given (backward), mc/lsc hold them per compact row;
 // padding rows get m = +inf so their replayed p is 0.
+// The same launch fills the per-position arrays that later kernels write at
+// the supervised positions only (each optional, N entries): the forward's
+// m = log s = -inf (the recurrence's initial state) and l = 0, the
+// backward's inverse map inv = -1.
+struct PosFill {
+  float* m = nullptr;
+  float* logs = nullptr;
+  float* row_loss = nullptr;
+  int* inv = nullptr;
+  int64_t N = 0;
+};
 template <typename T>
 __global__ __launch_bounds__(256) void k_gather(const T* __restrict__ H,
                                                 const int64_t* __restrict__ labels,
@@ -156,7 +211,14 @@ __global__ __launch_bounds__(256) void k_gather(const T* __restrict__ H,
                                                 int D, int64_t label_off, T* __restrict__ Hc, int* __restrict__ yc,
                                                 const float* __restrict__ m,
                                                 const float* __restrict__ logs, float* mc,
-                                                float* lsc) {
+                                                float* lsc, PosFill fill) {
+  for (int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; n < fill.N;
+       n += (int64_t)gridDim.x * blockDim.x) {
+    if (fill.m) fill.m[n] = -INFINITY;
+    if (fill.logs) fill.logs[n] = -INFINITY;
+    if (fill.row_loss) fill.row_loss[n] = 0.f;
+    if (fill.inv) fill.inv[n] = -1;
+  }
   constexpr int VEC = 16 / sizeof(T);
   const int vpr = D / VEC;
   const int64_t total = (int64_t)Cpad * vpr;
@@ -518,14 +580,17 @@ __global__ __launch_bounds__(1024) void k_loss_sum(const float* __restrict__ lro
 // the mean; the derivative of the chosen reduction otherwise):
 //   mean: lambda / C;  sum: lambda w_{idx_c} / div;  none: g_{idx_c} (per-row
 //   upstream gradient).  lambda = grad[0] (1 without grad).  Padding rows: 0.
+// The same launch completes the inverse map, inv[idx[c]] = c (the gather
+// set every entry to -1 before).
 __global__ void k_row_scale(const int32_t* __restrict__ idx, int C, int Cpad, int reduction,
                             const float* __restrict__ weights, float div, const float* __restrict__ grad,
-                            float* __restrict__ rsc) {
+                            float* __restrict__ rsc, int* __restrict__ inv) {
   const int c = blockIdx.x * blockDim.x + threadIdx.x;
   if (c >= Cpad) return;
   float r = 0.f;
   if (c < C) {
     const int n = idx[c];
+    inv[n] = c;
     if (reduction == kReduceNone) {
       r = grad ? grad[n] : 1.f;
     } else {
@@ -536,23 +601,20 @@ __global__ void k_row_scale(const int32_t* __restrict__ idx, int C, int Cpad, in
   rsc[c] = r;
 }
 
-__global__ void k_fill_f32(float* __restrict__ p, int64_t n, float v) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
-    p[i] = v;
-}
-__global__ void k_fill_i32(int* __restrict__ p, int64_t n, int v) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
-    p[i] = v;
+// m = log s = -inf and l = 0 at every position (each array optional).
+__global__ void k_fill_stats(float* __restrict__ m, float* __restrict__ logs, float* __restrict__ row_loss,
+                             int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    if (m) m[i] = -INFINITY;
+    if (logs) logs[i] = -INFINITY;
+    if (row_loss) row_loss[i] = 0.f;
+  }
 }
 // Zero n16 16-byte words (plus a byte tail).
 __global__ void k_zero(u32x4* __restrict__ p, int64_t n16, uint8_t* __restrict__ tail, int ntail) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (int64_t)gridDim.x * blockDim.x)
     p[i] = u32x4{0u, 0u, 0u, 0u};
   if (blockIdx.x == 0 && (int)threadIdx.x < ntail) tail[threadIdx.x] = 0;
-}
-__global__ void k_inv_scatter(const int32_t* __restrict__ idx, int C, int* __restrict__ inv) {
-  const int c = blockIdx.x * blockDim.x + threadIdx.x;
-  if (c < C) inv[idx[c]] = c;
 }
 __global__ void k_store_scalar(float* __restrict__ p, float v) { p[0] = v; }
 

@@ -139,6 +139,33 @@ def test_compaction_bit_exact_and_errors():
     assert r.status_c == _lib.LCE_OK and r.C == 299
 
 
+@pytest.mark.parametrize("N", [1, 8191, 8192, 8193, 65536, 65537, 200003])
+def test_compaction_sizes_bit_exact(N):
+    """Both compaction paths (one workgroup up to 65536 positions, three
+    launches above) at the boundaries of the one-workgroup rounds (8192
+    positions) and of the switch: indices and C bit-exact with the oracle,
+    entries past C untouched, and a bad label at the last position caught."""
+    say(f"[compaction] N={N}")
+    g = torch.Generator().manual_seed(7000 + N)
+    V = 1000
+    labels = torch.randint(0, V, (N,), generator=g, dtype=torch.int64)
+    labels[torch.rand(N, generator=g) < 0.3] = -100
+    mask = (torch.rand(N, generator=g) < 0.9).to(torch.uint8)
+    _, idx, C = O.supervised_rows(labels.numpy(), mask.numpy())
+    dev = "cuda:0"
+    ws = torch.empty(_lib.lce_forward_workspace_size(N, 8, V, torch.bfloat16), dtype=torch.uint8, device=dev)
+    out = torch.full((N,), -7, dtype=torch.int32, device=dev)
+    st, c = _lib.lce_compact_valid(labels.to(dev), mask.to(dev), V, -100, out, ws)
+    assert st == (_lib.LCE_OK if C > 0 else _lib.LCE_OK_EMPTY) and c == C
+    got = out.cpu().numpy()
+    np.testing.assert_array_equal(got[:C], idx)
+    assert np.all(got[C:] == -7)
+    bad, mb = labels.clone(), mask.clone()
+    bad[N - 1], mb[N - 1] = V, 1
+    st, _ = _lib.lce_compact_valid(bad.to(dev), mb.to(dev), V, -100, out, ws)
+    assert st == _lib.LCE_ERR_LABEL
+
+
 def test_nan_propagates():
     wl = WL.make_random(64, 32, 500, dtype=torch.float32, seed=11, ignore_frac=0.0)
     wl.H[5, 3] = float("nan")
